@@ -1,0 +1,111 @@
+"""CPU oracle for the GDN gating + gated delta-rule decode update.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the library and its Python binding
+never do, and nothing here imports them.  The arithmetic lives in
+``gdn_oracle.c`` (plain double-precision loops); this module only builds it
+with gcc and marshals numpy arrays into it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+_libs = {}
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (OpenMP across independent units only;
+    no fused multiply-add contraction, so each step rounds as written).
+    ``src``/``out`` let tests compile deliberately broken copies."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-ffp-contract=off", "-fno-fast-math", src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _load(path: str = _LIB):
+    lib = _libs.get(path)
+    if lib is None:
+        if path == _LIB and not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(path)
+        f = lib.gdn_oracle_update
+        P = ctypes.c_void_p
+        f.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                      ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                      ctypes.c_int, ctypes.c_int]
+        f.restype = ctypes.c_int
+        _libs[path] = lib
+    return lib
+
+
+def _ptr(arr: Optional[np.ndarray]):
+    return None if arr is None else arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
+           tokens_per_seq: int = 1, scale: float = 0.0, eps: float = 1e-6,
+           intermediates: bool = False, no_final_writeback: bool = False,
+           threads: int = 0, lib_path: str = _LIB):
+    """Run the oracle.  ``pool`` (float32 [slots, H_v, K, V]) is updated in
+    place.  Returns ``(out, inter)``: out is float64 [N, H_v, V] (rows of
+    untouched tokens stay NaN), inter is float32 [N, H_v, K, V] (NaN where not
+    written) or None.  ``lib_path`` selects another build of the same source."""
+    lib = _load(lib_path)
+    d = np.float64
+    q = np.ascontiguousarray(q, dtype=d)
+    k = np.ascontiguousarray(k, dtype=d)
+    v = np.ascontiguousarray(v, dtype=d)
+    a = np.ascontiguousarray(a, dtype=d)
+    b = np.ascontiguousarray(b, dtype=d)
+    A_log = np.ascontiguousarray(A_log, dtype=d)
+    dt_bias = np.ascontiguousarray(dt_bias, dtype=d)
+    idx = np.ascontiguousarray(state_idx, dtype=np.int32)
+    cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if pool.dtype != np.float32 or not pool.flags.c_contiguous:
+        raise ValueError("pool must be a C-contiguous float32 array (updated in place)")
+    N, Hk, K = q.shape
+    Hv, V = v.shape[1], v.shape[2]
+    if k.shape != q.shape or v.shape[0] != N or a.shape != (N, Hv) or b.shape != (N, Hv):
+        raise ValueError("inconsistent activation shapes")
+    if pool.shape[1:] != (Hv, K, V):
+        raise ValueError("pool shape must be [slots, H_v, K, V]")
+    out = np.full((N, Hv, V), np.nan, dtype=d)
+    inter = np.full((N, Hv, K, V), np.nan, dtype=np.float32) if intermediates else None
+    B = idx.shape[0]
+    rc = lib.gdn_oracle_update(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                               _ptr(A_log), _ptr(dt_bias), _ptr(pool), _ptr(idx),
+                               _ptr(cu), _ptr(out), _ptr(inter),
+                               B, tokens_per_seq, N, Hk, Hv, K, V, pool.shape[0],
+                               float(scale), float(eps), int(no_final_writeback),
+                               int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out, inter
+
+
+def run_inputs(inp, pool: np.ndarray, scale: float = 0.0, eps: float = 1e-6,
+               intermediates: Optional[bool] = None, no_final_writeback=False,
+               threads: int = 0):
+    """Run the oracle on a ``workloads.HostInputs`` bundle."""
+    wl = inp.wl
+    if intermediates is None:
+        intermediates = wl.intermediates
+    return update(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias,
+                  pool, inp.state_idx, inp.cu_seqlens,
+                  tokens_per_seq=wl.tokens_per_seq, scale=scale, eps=eps,
+                  intermediates=intermediates,
+                  no_final_writeback=no_final_writeback, threads=threads)
