@@ -1,0 +1,174 @@
+/*
+ * libgdn — fused sigmoid gating + gated delta-rule recurrent state update
+ * (Gated DeltaNet decode) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the fused kernel described by vLLM PR #35777
+ * ("implementation" section: the gating that produced g and beta is folded
+ * into the recurrent delta-rule update, which takes A_log, a, b and dt_bias
+ * directly, normalises q/k with rsqrt, and has a speculative-decoding mode)
+ * and tuned by sglang PR #18271 ("Benchmarking and Profiling": V-column
+ * tiles, bs=512 on a TP4 shard).  Per token t, value head h and key head
+ * j = h / G (G = H_v / H_k; consecutive v-heads share a k-head, as in the
+ * per-k-head a/b grouping of vLLM PR #37975, implementation section):
+ *
+ *   g     = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ *   beta  = sigmoid(b[t,h])
+ *   khat  = k[t,j] * rsqrt(|k[t,j]|^2 + eps)
+ *   qhat  = scale * q[t,j] * rsqrt(|q[t,j]|^2 + eps)      (scale default K^-1/2)
+ *   S     = exp(g) * S
+ *   u     = beta * (v[t,h] - S^T khat)
+ *   S     = S + khat u^T
+ *   out[t,h] = S^T qhat
+ *
+ * S is the K x V fp32 state of (sequence, v-head), gathered from and written
+ * back to a slot-indexed pool.  One call covers T=1 decode, fixed-T
+ * multi-token verification and varlen sequences (cu_seqlens), with optional
+ * per-token intermediate states.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers allocated by the caller; the
+ *    library never allocates, frees or synchronises device memory (except
+ *    GDN_FLAG_DEBUG_CHECKS, which copies the index arrays to the host).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns after the launch.
+ *  - Errors are returned as gdn_status before anything is launched; a
+ *    thread-local message (gdn_last_error_message) gives the detail.  No call
+ *    aborts or throws.
+ *  - The library keeps no state between calls and is re-entrant.  Calls that
+ *    update the same pool slots must be ordered by the caller (same stream).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL_POINTER = 1,      /* a required pointer is NULL              */
+    GDN_ERR_BAD_SHAPE = 2,         /* negative/inconsistent sizes, H_v % H_k  */
+    GDN_ERR_UNSUPPORTED_SHAPE = 3, /* K or V outside the supported set        */
+    GDN_ERR_UNSUPPORTED_DTYPE = 4, /* act_dtype not F32/BF16                  */
+    GDN_ERR_MISALIGNED = 5,        /* pointer or stride breaks the alignment  */
+    GDN_ERR_LAUNCH = 6,            /* the HIP runtime rejected the launch     */
+    GDN_ERR_BAD_ARGUMENT = 7,      /* other invalid argument (tile override,
+                                      debug-check contract violation, ...)    */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_F32 = 0,
+    GDN_DTYPE_BF16 = 1,
+} gdn_dtype;
+
+/* Leave the pool unchanged (spec verify whose acceptance is decided later:
+ * the caller copies the accepted intermediate state itself). */
+#define GDN_FLAG_NO_FINAL_WRITEBACK 0x1u
+/* Before launching, copy state_idx (and cu_seqlens) to the host and check
+ * the caller contract: non-negative slots distinct and < num_slots,
+ * cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = num_tokens.  Synchronous
+ * on `stream`; meant for tests and debugging. */
+#define GDN_FLAG_DEBUG_CHECKS 0x2u
+
+typedef struct gdn_config {
+    int32_t num_seqs;        /* B >= 0 sequences (B = 0: nothing is launched)   */
+    int32_t tokens_per_seq;  /* T >= 1 tokens per sequence when cu_seqlens is
+                                NULL (sequence i owns token rows [i*T, i*T+T));
+                                ignored with cu_seqlens                          */
+    int64_t num_tokens;      /* N: rows of q, k, v, a, b, out, intermediate_states.
+                                >= B*T without cu_seqlens; = cu_seqlens[B] with */
+    int32_t num_k_heads;     /* H_k >= 1                                         */
+    int32_t num_v_heads;     /* H_v >= 1, a multiple of H_k                      */
+    int32_t head_k_dim;      /* K in {32, 64, 128, 256}                          */
+    int32_t head_v_dim;      /* V in {32, 64, 128, 256}                          */
+    int64_t num_slots;       /* rows of the state pool (bounds the slot indices) */
+    int32_t act_dtype;       /* gdn_dtype of q, k, v, a, b and out               */
+    float scale;             /* query scale; <= 0 selects K^-1/2                 */
+    float l2norm_eps;        /* eps inside the rsqrt of the q/k norms (>= 0)     */
+    int64_t q_stride_tok;    /* elements between consecutive tokens of q;
+                                0 = dense (H_k*K).  Heads are dense within a token */
+    int64_t k_stride_tok;    /* same for k                                       */
+    int64_t v_stride_tok;    /* same for v (dense = H_v*V)                       */
+    uint32_t flags;          /* GDN_FLAG_*                                       */
+    int32_t block_v;         /* V-columns per wavefront tile: 0 = library choice,
+                                else 8, 16, 32 or 64 (dividing V)                */
+    int32_t waves_per_group; /* wavefronts per workgroup: 0 = library choice,
+                                else 1..8, dividing G*V/block_v                  */
+} gdn_config;
+
+/* Describes the launch that a configuration maps to (gdn_plan). */
+typedef struct gdn_launch_info {
+    int32_t block_v;          /* V-columns per wavefront                     */
+    int32_t waves_per_group;  /* wavefronts per workgroup                    */
+    int32_t tokens_per_chunk; /* tokens staged in LDS at a time              */
+    int32_t multi_token;      /* 0: single-token decode kernel; 1: token loop */
+    int64_t workgroups;       /* grid size                                   */
+    int32_t threads_per_group;
+    int32_t lds_bytes;        /* dynamic LDS per workgroup                   */
+} gdn_launch_info;
+
+/* Fills `cfg` with defaults: scale 0 (K^-1/2), eps 1e-6, dense strides,
+ * F32 activations, T = 1, library-chosen tiling. Sizes are zeroed. */
+void gdn_default_config(gdn_config* cfg);
+
+/*
+ * The fused gating + gated delta-rule update (one launch).
+ *
+ *  q, k     [N, H_k, K]   act_dtype; token stride q/k_stride_tok elements
+ *  v        [N, H_v, V]   act_dtype; token stride v_stride_tok
+ *  a, b     [N, H_v]      act_dtype, dense
+ *  A_log, dt_bias [H_v]   fp32
+ *  state_pool [num_slots, H_v, K, V] fp32, V fastest; updated in place
+ *  state_idx  [B] int32: pool slot of sequence i; any negative value marks a
+ *             padded sequence, which is skipped entirely (its pool rows, out
+ *             rows and intermediate rows are neither read nor written)
+ *  cu_seqlens [B+1] int32 token offsets, or NULL for T tokens per sequence.
+ *             A zero-length sequence is skipped like a padded one.
+ *  out      [N, H_v, V]   act_dtype, dense; bf16 is rounded to nearest even
+ *  intermediate_states [N, H_v, K, V] fp32 or NULL: row t receives S after
+ *             token t (so the last token's row equals the final state)
+ *
+ * Alignment: q, k, v, out, state_pool and intermediate_states 16-byte
+ * aligned; q/k/v token strides multiples of 8 elements.
+ * Caller contract (undefined if broken; checked under GDN_FLAG_DEBUG_CHECKS):
+ * non-negative slot indices are distinct and < num_slots; cu_seqlens is
+ * non-decreasing from 0 to N.  Rows of out/intermediate_states that belong to
+ * no live token are not written.
+ */
+gdn_status gdn_gating_delta_rule_update(
+    const void* q, const void* k, const void* v, const void* a, const void* b,
+    const float* A_log, const float* dt_bias, float* state_pool,
+    const int32_t* state_idx, const int32_t* cu_seqlens, void* out,
+    float* intermediate_states, const gdn_config* cfg, void* stream);
+
+/* Host-side argument check of gdn_gating_delta_rule_update (same arguments,
+ * no stream); launches nothing and never touches device memory. */
+gdn_status gdn_validate(
+    const void* q, const void* k, const void* v, const void* a, const void* b,
+    const float* A_log, const float* dt_bias, const float* state_pool,
+    const int32_t* state_idx, const int32_t* cu_seqlens, const void* out,
+    const float* intermediate_states, const gdn_config* cfg);
+
+/* The launch a valid configuration maps to (no device access). */
+gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens,
+                    gdn_launch_info* info);
+
+/* Static description of a status code (never NULL). */
+const char* gdn_status_string(gdn_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* gdn_last_error_message(void);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

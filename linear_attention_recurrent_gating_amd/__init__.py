@@ -1,0 +1,243 @@
+"""Python binding of libgdn: the fused sigmoid-gating + gated delta-rule state
+update (Gated DeltaNet decode) on AMD MI355X.
+
+Argument marshalling only.  Every step of the update runs in the HIP kernels
+of ``_lib/libgdn.so`` behind the C-ABI declared in ``include/gdn.h``; PyTorch
+supplies device memory and the stream.  The library is loaded on first use,
+and every entry point raises ImportError when it has not been built
+(``python -m linear_attention_recurrent_gating_amd.build``); there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libgdn.so")
+
+GDN_OK = 0
+GDN_DTYPE_F32 = 0
+GDN_DTYPE_BF16 = 1
+GDN_FLAG_NO_FINAL_WRITEBACK = 0x1
+GDN_FLAG_DEBUG_CHECKS = 0x2
+
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
+                3: "GDN_ERR_UNSUPPORTED_SHAPE", 4: "GDN_ERR_UNSUPPORTED_DTYPE",
+                5: "GDN_ERR_MISALIGNED", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_BAD_ARGUMENT"}
+
+# Every symbol include/gdn.h declares.
+EXPORTED = ("gdn_default_config", "gdn_gating_delta_rule_update", "gdn_validate", "gdn_plan",
+            "gdn_status_string", "gdn_last_error_message", "gdn_abi_version")
+
+
+class GdnConfig(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("tokens_per_seq", ctypes.c_int32),
+                ("num_tokens", ctypes.c_int64), ("num_k_heads", ctypes.c_int32),
+                ("num_v_heads", ctypes.c_int32), ("head_k_dim", ctypes.c_int32),
+                ("head_v_dim", ctypes.c_int32), ("num_slots", ctypes.c_int64),
+                ("act_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("l2norm_eps", ctypes.c_float), ("q_stride_tok", ctypes.c_int64),
+                ("k_stride_tok", ctypes.c_int64), ("v_stride_tok", ctypes.c_int64),
+                ("flags", ctypes.c_uint32), ("block_v", ctypes.c_int32),
+                ("waves_per_group", ctypes.c_int32)]
+
+
+class GdnLaunchInfo(ctypes.Structure):
+    _fields_ = [("block_v", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+                ("tokens_per_chunk", ctypes.c_int32), ("multi_token", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64), ("threads_per_group", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libgdn is not built ({LIB_PATH} missing): run "
+                          "`python -m linear_attention_recurrent_gating_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, C = ctypes.c_void_p, ctypes.POINTER(GdnConfig)
+    lib.gdn_default_config.argtypes = [C]
+    lib.gdn_default_config.restype = None
+    lib.gdn_gating_delta_rule_update.argtypes = [P] * 12 + [C, P]
+    lib.gdn_gating_delta_rule_update.restype = ctypes.c_int
+    lib.gdn_validate.argtypes = [P] * 12 + [C]
+    lib.gdn_validate.restype = ctypes.c_int
+    lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
+    lib.gdn_plan.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error_message.argtypes = []
+    lib.gdn_last_error_message.restype = ctypes.c_char_p
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_abi_version.restype = ctypes.c_int
+    return lib
+
+
+_LIB_HANDLE: Optional[ctypes.CDLL] = None
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded C library (loaded on first use)."""
+    global _LIB_HANDLE
+    if _LIB_HANDLE is None:
+        _LIB_HANDLE = _load()
+    return _LIB_HANDLE
+
+
+def gdn_abi_version() -> int:
+    return raw_library().gdn_abi_version()
+
+
+def gdn_status_string(status: int) -> str:
+    return raw_library().gdn_status_string(status).decode()
+
+
+def gdn_last_error_message() -> str:
+    return raw_library().gdn_last_error_message().decode()
+
+
+def gdn_default_config() -> GdnConfig:
+    cfg = GdnConfig()
+    raw_library().gdn_default_config(ctypes.byref(cfg))
+    return cfg
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, gdn_last_error_message() or gdn_status_string(status))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
+                   intermediate_states):
+    """dtype/shape/device/layout checks the C-ABI cannot make on raw pointers."""
+    import torch
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise ValueError("q, k must be [N, H_k, K] and v [N, H_v, V] with the same N")
+    N, Hv, V = v.shape
+    K = q.shape[2]
+    act = q.dtype
+    if act not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"activations must be float32 or bfloat16, got {act}")
+    for name, t in (("k", k), ("v", v), ("a", a), ("b", b), ("out", out)):
+        if t.dtype != act:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {act} like q")
+    for name, t, shape in (("a", a, (N, Hv)), ("b", b, (N, Hv)), ("out", out, (N, Hv, V))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {list(shape)} tensor")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (Hv,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [{Hv}] tensor")
+    if (state_pool.dtype != torch.float32 or state_pool.dim() != 4
+            or tuple(state_pool.shape[1:]) != (Hv, K, V) or not state_pool.is_contiguous()):
+        raise ValueError(f"state_pool must be a contiguous float32 [slots, {Hv}, {K}, {V}] tensor")
+    if state_idx.dtype != torch.int32 or state_idx.dim() != 1 or not state_idx.is_contiguous():
+        raise ValueError("state_idx must be a contiguous int32 [B] tensor")
+    B = state_idx.shape[0]
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32
+                                   or tuple(cu_seqlens.shape) != (B + 1,)
+                                   or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor")
+    if intermediate_states is not None and (
+            intermediate_states.dtype != torch.float32
+            or tuple(intermediate_states.shape) != (N, Hv, K, V)
+            or not intermediate_states.is_contiguous()):
+        raise ValueError("intermediate_states must be a contiguous float32 [N, H_v, K, V] tensor")
+    dev = q.device
+    for t in (k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
+              intermediate_states):
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU (ROCm device)")
+
+
+def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=None,
+                scale: float = 0.0, eps: float = 1e-6, flags: int = 0, block_v: int = 0,
+                waves_per_group: int = 0, k=None) -> GdnConfig:
+    """Sizes and strides of a call, read off the tensors' shapes."""
+    import torch
+    N, Hk, K = q.shape
+    Hv, V = v.shape[1], v.shape[2]
+    B = state_idx.shape[0]
+    if tokens_per_seq is None:
+        tokens_per_seq = N // B if (cu_seqlens is None and B > 0) else 1
+    cfg = gdn_default_config()
+    cfg.num_seqs = B
+    cfg.tokens_per_seq = tokens_per_seq
+    cfg.num_tokens = N
+    cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim = Hk, Hv, K, V
+    cfg.num_slots = state_pool.shape[0]
+    if q.dtype == torch.bfloat16:
+        cfg.act_dtype = GDN_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        cfg.act_dtype = GDN_DTYPE_F32
+    else:
+        cfg.act_dtype = -1  # rejected by the library with GDN_ERR_UNSUPPORTED_DTYPE
+    cfg.scale = scale
+    cfg.l2norm_eps = eps
+    for name, t in (("q_stride_tok", q), ("k_stride_tok", q if k is None else k), ("v_stride_tok", v)):
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError("heads must be dense within a token (strides [*, D, 1])")
+        setattr(cfg, name, t.stride(0) if t.shape[0] > 1 else 0)
+    cfg.flags = flags
+    cfg.block_v = block_v
+    cfg.waves_per_group = waves_per_group
+    return cfg
+
+
+def gdn_gating_delta_rule_update(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx,
+                                 cu_seqlens=None, out=None, intermediate_states=None, *,
+                                 tokens_per_seq=None, scale: float = 0.0, eps: float = 1e-6,
+                                 flags: int = 0, block_v: int = 0, waves_per_group: int = 0,
+                                 stream=None):
+    """Enqueue the fused update on ``stream`` (default: torch's current stream
+    on q's device).  Shapes: q, k [N, H_k, K]; v [N, H_v, V]; a, b [N, H_v];
+    A_log, dt_bias [H_v] fp32; state_pool [slots, H_v, K, V] fp32 (updated in
+    place); state_idx [B] int32; cu_seqlens [B+1] int32 or None; out [N, H_v, V]
+    (allocated like v when None); intermediate_states [N, H_v, K, V] fp32 or
+    None.  Returns ``out``."""
+    import torch
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
+                   intermediate_states)
+    cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
+                      scale=scale, eps=eps, flags=flags, block_v=block_v,
+                      waves_per_group=waves_per_group, k=k)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(raw_library().gdn_gating_delta_rule_update(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out),
+        _ptr(intermediate_states), ctypes.byref(cfg), stream))
+    return out
+
+
+def gdn_validate(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens=None,
+                 out=None, intermediate_states=None, cfg: Optional[GdnConfig] = None, **kw) -> int:
+    """Host-only argument check; returns the gdn_status code."""
+    if cfg is None:
+        cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, k=k, **kw)
+    return raw_library().gdn_validate(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                             _ptr(dt_bias), _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens),
+                             _ptr(out), _ptr(intermediate_states), ctypes.byref(cfg))
+
+
+def gdn_plan(cfg: GdnConfig, has_cu_seqlens: bool) -> GdnLaunchInfo:
+    info = GdnLaunchInfo()
+    _check(raw_library().gdn_plan(ctypes.byref(cfg), int(bool(has_cu_seqlens)), ctypes.byref(info)))
+    return info
+

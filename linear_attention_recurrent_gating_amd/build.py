@@ -1,0 +1,57 @@
+"""Builds libgdn (HIP kernels + C-ABI host code) in-tree for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(LIBDIR, "libgdn.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM_INCLUDE = "/opt/rocm/include"
+
+DEVICE_SOURCES = ["gdn_kernels.hip"]
+HOST_SOURCES = ["gdn_api.cpp"]
+
+# Packed fp32 VALU forms are disabled: hipcc -O3 otherwise forms them from
+# scalar float code.  No implicit FMA contraction: the kernels spell out every
+# fused multiply-add, so all instances round the same way.
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+DEVICE = ["-x", "hip", "--offload-arch=gfx950", "-ffp-contract=off", "-Xclang", "-target-feature",
+          "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, extra_device_flags=()) -> str:
+    os.makedirs(LIBDIR, exist_ok=True)
+    objs = []
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(LIBDIR, src + ".o")
+        _run([HIPCC, *COMMON, *DEVICE, *extra_device_flags, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(LIBDIR, src + ".o")
+        _run([HIPCC, *COMMON, "-I", ROCM_INCLUDE, "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
+              os.path.join(CSRC, src),
+              "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,303 @@
+// C-ABI of libgdn: argument validation, the tile table and the launch.
+// The operation and its conventions are documented in include/gdn.h.
+
+#include "gdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+int default_block_v(const gdn_config& c) {
+    // One 128-byte line per row segment: 32 fp32 columns, the widest tile
+    // whose K x BV slice stays at 64 VGPRs for K = 128.
+    int bv = 32;
+    while (bv > 8 && (c.head_v_dim % bv != 0 || !gdn::instance_exists(c.head_k_dim, bv))) bv /= 2;
+    return bv;
+}
+
+// Largest divisor of `units` (wave units per k-head) not above 8.
+int default_waves(int units) {
+    for (int w = 8; w >= 1; --w)
+        if (units % w == 0) return w;
+    return 1;
+}
+
+gdn_status check_config(const gdn_config* cfg, bool has_cu) {
+    if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
+    const gdn_config& c = *cfg;
+    if (c.num_seqs < 0) return fail(GDN_ERR_BAD_SHAPE, "num_seqs = %d < 0", c.num_seqs);
+    if (c.num_k_heads < 1 || c.num_v_heads < 1)
+        return fail(GDN_ERR_BAD_SHAPE, "head counts must be >= 1 (H_k=%d, H_v=%d)", c.num_k_heads,
+                    c.num_v_heads);
+    if (c.num_v_heads % c.num_k_heads != 0)
+        return fail(GDN_ERR_BAD_SHAPE, "H_v=%d is not a multiple of H_k=%d", c.num_v_heads,
+                    c.num_k_heads);
+    if (!supported_dim(c.head_k_dim) || !supported_dim(c.head_v_dim))
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE, "K=%d, V=%d: each must be 32, 64, 128 or 256",
+                    c.head_k_dim, c.head_v_dim);
+    if (c.act_dtype != GDN_DTYPE_F32 && c.act_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_UNSUPPORTED_DTYPE, "act_dtype %d is neither F32 nor BF16", c.act_dtype);
+    if (c.num_tokens < 0) return fail(GDN_ERR_BAD_SHAPE, "num_tokens < 0");
+    if (c.num_tokens > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "num_tokens exceeds 2^31-1");
+    if (!has_cu) {
+        if (c.tokens_per_seq < 1)
+            return fail(GDN_ERR_BAD_SHAPE, "tokens_per_seq = %d < 1 without cu_seqlens",
+                        c.tokens_per_seq);
+        if (static_cast<int64_t>(c.num_seqs) * c.tokens_per_seq > c.num_tokens)
+            return fail(GDN_ERR_BAD_SHAPE, "num_seqs*tokens_per_seq = %lld exceeds num_tokens = %lld",
+                        static_cast<long long>(c.num_seqs) * c.tokens_per_seq,
+                        static_cast<long long>(c.num_tokens));
+    }
+    if (c.num_slots < 1) return fail(GDN_ERR_BAD_SHAPE, "num_slots must be >= 1");
+    if (!std::isfinite(c.scale)) return fail(GDN_ERR_BAD_ARGUMENT, "scale is not finite");
+    if (!(c.l2norm_eps >= 0.0f) || !std::isfinite(c.l2norm_eps))
+        return fail(GDN_ERR_BAD_ARGUMENT, "l2norm_eps must be finite and >= 0");
+    const int64_t qk_dense = static_cast<int64_t>(c.num_k_heads) * c.head_k_dim;
+    const int64_t v_dense = static_cast<int64_t>(c.num_v_heads) * c.head_v_dim;
+    struct { const char* name; int64_t s; int64_t dense; } strides[] = {
+        {"q_stride_tok", c.q_stride_tok, qk_dense},
+        {"k_stride_tok", c.k_stride_tok, qk_dense},
+        {"v_stride_tok", c.v_stride_tok, v_dense}};
+    for (const auto& st : strides) {
+        if (st.s == 0) continue;
+        if (st.s < st.dense)
+            return fail(GDN_ERR_BAD_SHAPE, "%s = %lld is below the dense row size %lld", st.name,
+                        static_cast<long long>(st.s), static_cast<long long>(st.dense));
+        if (st.s % 8 != 0)
+            return fail(GDN_ERR_MISALIGNED, "%s = %lld is not a multiple of 8 elements", st.name,
+                        static_cast<long long>(st.s));
+    }
+    const int G = c.num_v_heads / c.num_k_heads;
+    if (c.block_v != 0) {
+        if (c.block_v != 8 && c.block_v != 16 && c.block_v != 32 && c.block_v != 64)
+            return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d is not 8, 16, 32 or 64", c.block_v);
+        if (c.head_v_dim % c.block_v != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d does not divide V = %d", c.block_v,
+                        c.head_v_dim);
+        if (!gdn::instance_exists(c.head_k_dim, c.block_v))
+            return fail(GDN_ERR_BAD_ARGUMENT, "no kernel for K = %d with block_v = %d", c.head_k_dim,
+                        c.block_v);
+    }
+    const int bv = c.block_v ? c.block_v : default_block_v(c);
+    const int units = G * (c.head_v_dim / bv);
+    if (c.waves_per_group != 0) {
+        if (c.waves_per_group < 1 || c.waves_per_group > 8 || units % c.waves_per_group != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT,
+                        "waves_per_group = %d must be in 1..8 and divide G*V/block_v = %d",
+                        c.waves_per_group, units);
+    }
+    const int w = c.waves_per_group ? c.waves_per_group : default_waves(units);
+    const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / w);
+    if (groups > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
+                                        static_cast<long long>(groups));
+    return GDN_OK;
+}
+
+void make_shape(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    s.K = c.head_k_dim;
+    s.block_v = c.block_v ? c.block_v : default_block_v(c);
+    s.act = c.act_dtype;
+    s.multi_token = (has_cu || c.tokens_per_seq > 1) ? 1 : 0;
+    const int units = G * (c.head_v_dim / s.block_v);
+    s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+    s.chunk = s.multi_token ? gdn::kChunkTokens : 1;
+    s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
+    s.lds_bytes = gdn::lds_bytes_for(s.K, s.block_v, s.waves, s.chunk, s.multi_token);
+}
+
+gdn_status debug_check_indices(const gdn_config& c, const int32_t* state_idx,
+                               const int32_t* cu_seqlens, hipStream_t stream) {
+    const int B = c.num_seqs;
+    std::vector<int32_t> idx(B), cu(cu_seqlens ? B + 1 : 0);
+    if (hipMemcpyAsync(idx.data(), state_idx, sizeof(int32_t) * B, hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "debug checks: copying state_idx failed");
+    if (cu_seqlens &&
+        hipMemcpyAsync(cu.data(), cu_seqlens, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "debug checks: copying cu_seqlens failed");
+    if (hipStreamSynchronize(stream) != hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "debug checks: stream synchronisation failed");
+    std::vector<char> seen(static_cast<size_t>(c.num_slots), 0);
+    for (int i = 0; i < B; ++i) {
+        if (idx[i] < 0) continue;
+        if (idx[i] >= c.num_slots)
+            return fail(GDN_ERR_BAD_ARGUMENT, "state_idx[%d] = %d is not below num_slots = %lld", i,
+                        idx[i], static_cast<long long>(c.num_slots));
+        if (seen[idx[i]]) return fail(GDN_ERR_BAD_ARGUMENT, "slot %d is used twice", idx[i]);
+        seen[idx[i]] = 1;
+    }
+    if (cu_seqlens) {
+        if (cu[0] != 0) return fail(GDN_ERR_BAD_ARGUMENT, "cu_seqlens[0] = %d, not 0", cu[0]);
+        for (int i = 0; i < B; ++i)
+            if (cu[i + 1] < cu[i])
+                return fail(GDN_ERR_BAD_ARGUMENT, "cu_seqlens decreases at %d", i);
+        if (cu[B] != c.num_tokens)
+            return fail(GDN_ERR_BAD_ARGUMENT, "cu_seqlens[B] = %d differs from num_tokens = %lld",
+                        cu[B], static_cast<long long>(c.num_tokens));
+    }
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gdn_default_config(gdn_config* cfg) {
+    if (!cfg) return;
+    std::memset(cfg, 0, sizeof(*cfg));
+    cfg->tokens_per_seq = 1;
+    cfg->act_dtype = GDN_DTYPE_F32;
+    cfg->scale = 0.0f;
+    cfg->l2norm_eps = 1e-6f;
+}
+
+gdn_status gdn_validate(const void* q, const void* k, const void* v, const void* a, const void* b,
+                        const float* A_log, const float* dt_bias, const float* state_pool,
+                        const int32_t* state_idx, const int32_t* cu_seqlens, const void* out,
+                        const float* intermediate_states, const gdn_config* cfg) {
+    g_last_error[0] = '\0';
+    gdn_status s = check_config(cfg, cu_seqlens != nullptr);
+    if (s != GDN_OK) return s;
+    if (cfg->num_seqs == 0) return GDN_OK;
+    const size_t esize = cfg->act_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    struct { const void* p; const char* name; size_t align; } ptrs[] = {
+        {q, "q", 16}, {k, "k", 16}, {v, "v", 16}, {a, "a", esize}, {b, "b", esize},
+        {A_log, "A_log", 4}, {dt_bias, "dt_bias", 4}, {state_pool, "state_pool", 16},
+        {state_idx, "state_idx", 4}, {out, "out", 16}};
+    for (const auto& e : ptrs) {
+        if (!e.p) return fail(GDN_ERR_NULL_POINTER, "%s is NULL", e.name);
+        if (!aligned(e.p, e.align))
+            return fail(GDN_ERR_MISALIGNED, "%s is not %zu-byte aligned", e.name, e.align);
+    }
+    if (cu_seqlens && !aligned(cu_seqlens, 4))
+        return fail(GDN_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
+    if (intermediate_states && !aligned(intermediate_states, 16))
+        return fail(GDN_ERR_MISALIGNED, "intermediate_states is not 16-byte aligned");
+    return GDN_OK;
+}
+
+gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* info) {
+    g_last_error[0] = '\0';
+    if (!info) return fail(GDN_ERR_NULL_POINTER, "info is NULL");
+    gdn_status s = check_config(cfg, has_cu_seqlens != 0);
+    if (s != GDN_OK) return s;
+    gdn::LaunchShape sh{};
+    make_shape(*cfg, has_cu_seqlens != 0, sh);
+    info->block_v = sh.block_v;
+    info->waves_per_group = sh.waves;
+    info->tokens_per_chunk = sh.chunk;
+    info->multi_token = sh.multi_token;
+    info->workgroups = sh.groups;
+    info->threads_per_group = sh.waves * 64;
+    info->lds_bytes = sh.lds_bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void* v, const void* a,
+                                        const void* b, const float* A_log, const float* dt_bias,
+                                        float* state_pool, const int32_t* state_idx,
+                                        const int32_t* cu_seqlens, void* out,
+                                        float* intermediate_states, const gdn_config* cfg,
+                                        void* stream) {
+    gdn_status s = gdn_validate(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens,
+                                out, intermediate_states, cfg);
+    if (s != GDN_OK) return s;
+    const gdn_config& c = *cfg;
+    if (c.num_seqs == 0) return GDN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c.flags & GDN_FLAG_DEBUG_CHECKS) {
+        s = debug_check_indices(c, state_idx, cu_seqlens, st);
+        if (s != GDN_OK) return s;
+    }
+    const bool has_cu = cu_seqlens != nullptr;
+    gdn::LaunchShape sh{};
+    make_shape(c, has_cu, sh);
+
+    gdn::FusedParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.pool = state_pool;
+    p.state_idx = state_idx;
+    p.cu_seqlens = cu_seqlens;
+    p.out = out;
+    p.inter = intermediate_states;
+    const int64_t qk_dense = static_cast<int64_t>(c.num_k_heads) * c.head_k_dim;
+    p.q_stride = c.q_stride_tok ? c.q_stride_tok : qk_dense;
+    p.k_stride = c.k_stride_tok ? c.k_stride_tok : qk_dense;
+    p.v_stride = c.v_stride_tok ? c.v_stride_tok : static_cast<int64_t>(c.num_v_heads) * c.head_v_dim;
+    p.T = has_cu ? 0 : c.tokens_per_seq;
+    p.Hk = c.num_k_heads;
+    p.Hv = c.num_v_heads;
+    p.G = c.num_v_heads / c.num_k_heads;
+    p.V = c.head_v_dim;
+    p.groups_per_khead = (p.G * (c.head_v_dim / sh.block_v)) / sh.waves;
+    p.scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt(static_cast<float>(c.head_k_dim));
+    p.eps = c.l2norm_eps;
+    p.write_final = (c.flags & GDN_FLAG_NO_FINAL_WRITEBACK) ? 0 : 1;
+
+    static const bool log = [] {
+        const char* e = std::getenv("GDN_LOG");
+        return e && e[0] == '1';
+    }();
+    if (log)
+        std::fprintf(stderr,
+                     "[gdn] K=%d V=%d act=%s multi_token=%d block_v=%d waves=%d chunk=%d groups=%lld "
+                     "lds=%d\n",
+                     sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", sh.multi_token, sh.block_v,
+                     sh.waves, sh.chunk, static_cast<long long>(sh.groups), sh.lds_bytes);
+
+    const hipError_t e = gdn::launch_fused(sh, p, st);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
+const char* gdn_status_string(gdn_status status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case GDN_ERR_BAD_SHAPE: return "inconsistent or invalid sizes";
+        case GDN_ERR_UNSUPPORTED_SHAPE: return "unsupported head dimension";
+        case GDN_ERR_UNSUPPORTED_DTYPE: return "unsupported activation dtype";
+        case GDN_ERR_MISALIGNED: return "pointer or stride misaligned";
+        case GDN_ERR_LAUNCH: return "kernel launch failed";
+        case GDN_ERR_BAD_ARGUMENT: return "invalid argument";
+    }
+    return "unknown status";
+}
+
+const char* gdn_last_error_message(void) { return g_last_error; }
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+}  // extern "C"

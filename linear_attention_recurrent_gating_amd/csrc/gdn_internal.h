@@ -1,0 +1,62 @@
+// Internal interface between the C-ABI host code (gdn_api.cpp) and the
+// device code (gdn_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Everything one launch of the fused update needs.  Passed by value as the
+// kernel argument.
+struct FusedParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* a;
+    const void* b;
+    const float* A_log;
+    const float* dt_bias;
+    float* pool;
+    const int32_t* state_idx;
+    const int32_t* cu_seqlens;  // nullptr: T tokens per sequence
+    void* out;
+    float* inter;               // nullptr: no intermediate states
+    int64_t q_stride;           // elements between tokens
+    int64_t k_stride;
+    int64_t v_stride;
+    int32_t T;
+    int32_t Hk;
+    int32_t Hv;
+    int32_t G;                  // Hv / Hk
+    int32_t V;
+    int32_t groups_per_khead;   // workgroups per (sequence, k-head)
+    float scale;
+    float eps;
+    int32_t write_final;        // 0 under GDN_FLAG_NO_FINAL_WRITEBACK
+};
+
+struct LaunchShape {
+    int K;
+    int block_v;
+    int act;          // 0 = fp32, 1 = bf16
+    int multi_token;  // 0: one token per sequence; 1: chunked token loop
+    int waves;        // wavefronts per workgroup
+    int chunk;        // tokens staged per chunk (1 for the single-token kernel)
+    int64_t groups;   // grid size
+    int lds_bytes;
+};
+
+// Tokens staged in LDS at a time by the multi-token kernel.
+constexpr int kChunkTokens = 16;
+
+// Dynamic LDS bytes of a launch shape.
+int lds_bytes_for(int K, int block_v, int waves, int chunk, int multi_token);
+
+// True when a kernel instance exists for (K, block_v).
+bool instance_exists(int K, int block_v);
+
+// Enqueues the fused kernel; returns the HIP launch status.
+hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);
+
+}  // namespace gdn

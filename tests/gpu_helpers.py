@@ -1,0 +1,108 @@
+"""Shared helpers of the GPU parity tests: run the HIP path and the oracle on
+the same seeded inputs and compare them."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from linear_attention_recurrent_gating_amd import workloads as W
+
+# Tolerances on max|x - ref| / max|ref|, per compared tensor.
+TOL_F32 = 1e-4      # fp32 activations
+TOL_BF16 = 2e-2     # bf16 q/k/v/a/b with fp32 state
+# Guard on the fp32 state with bf16 activations: the kernel widens the same
+# bf16 values the oracle gets, so only fp32 arithmetic separates the states;
+# a wrong state carry would show far above this.
+TOL_STATE_GUARD = 1e-4
+
+
+def announce(msg: str):
+    """Names the case on the real stderr (not captured) before GPU work."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def rel_err(x, ref) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape, (x.shape, ref.shape)
+    if x.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(x - ref)))
+    if not np.isfinite(err):
+        return float("inf")
+    return err / scale if scale > 0 else err
+
+
+def tol_for(wl) -> float:
+    return TOL_BF16 if wl.act == W.ACT_BF16 else TOL_F32
+
+
+def to_np(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def live_rows(inp):
+    """Token rows of live (non-padded) sequences, and of padded ones."""
+    starts = np.concatenate([[0], np.cumsum(inp.lengths)[:-1]]).astype(np.int64)
+    live, dead = [], []
+    for i, (s, L) in enumerate(zip(starts, inp.lengths)):
+        (live if inp.state_idx[i] >= 0 else dead).append(np.arange(s, s + L))
+    cat = lambda xs: np.concatenate(xs) if xs else np.zeros(0, np.int64)
+    return cat(live), cat(dead)
+
+
+def run_gpu(inp, pool, device, intermediates=None, flags=0, block_v=0, waves_per_group=0,
+            tensors=None, stream=None):
+    """One call of the HIP path.  Returns (out, inter) as torch tensors; rows
+    that must not be written are pre-filled with NaN."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    wl = inp.wl
+    d = tensors if tensors is not None else W.to_torch(inp, device)
+    if intermediates is None:
+        intermediates = wl.intermediates
+    act = torch.bfloat16 if wl.act == W.ACT_BF16 else torch.float32
+    N = inp.num_tokens
+    out = torch.full((N, wl.num_v_heads, wl.head_v_dim), float("nan"), dtype=act, device=device)
+    inter = None
+    if intermediates:
+        inter = torch.full((N, wl.num_v_heads, wl.head_k_dim, wl.head_v_dim), float("nan"),
+                           dtype=torch.float32, device=device)
+    gdn.gdn_gating_delta_rule_update(
+        d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool, d["state_idx"],
+        d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq, flags=flags,
+        block_v=block_v, waves_per_group=waves_per_group, stream=stream)
+    torch.cuda.synchronize()
+    return out, inter
+
+
+def sub_inputs(inp, seqs):
+    """The sub-batch of sequences `seqs` (with their token rows), re-slotted to
+    0..len(seqs)-1, for the oracle."""
+    starts = np.concatenate([[0], np.cumsum(inp.lengths)[:-1]]).astype(np.int64)
+    rows = np.concatenate([np.arange(starts[i], starts[i] + inp.lengths[i]) for i in seqs]) \
+        if len(seqs) else np.zeros(0, np.int64)
+    lengths = inp.lengths[seqs]
+    cu = np.zeros(len(seqs) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    idx = np.where(inp.state_idx[seqs] >= 0, np.arange(len(seqs)), -1).astype(np.int32)
+    return dict(q=inp.q[rows], k=inp.k[rows], v=inp.v[rows], a=inp.a[rows], b=inp.b[rows],
+                A_log=inp.A_log, dt_bias=inp.dt_bias, state_idx=idx, cu_seqlens=cu), rows
+
+
+def oracle_on_seqs(inp, pool0_rows, seqs, intermediates=False, no_final_writeback=False):
+    """Oracle on the sequences `seqs`; pool0_rows [len(seqs), H_v, K, V] holds
+    their initial states.  Returns (out rows, final states, inter rows, rows)."""
+    d, rows = sub_inputs(inp, seqs)
+    pool = np.ascontiguousarray(pool0_rows, dtype=np.float32).copy()
+    out, inter = oracle.update(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                               pool, d["state_idx"], d["cu_seqlens"], intermediates=intermediates,
+                               no_final_writeback=no_final_writeback)
+    return out, pool, inter, rows

@@ -1,0 +1,185 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-side validation and planning behave as documented.
+No call here launches a kernel or touches device memory (validation and
+planning never dereference the pointers they are given)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_recurrent_gating_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+# Fake, never-dereferenced device addresses (16-byte aligned).
+A = [0x7f0000000000 + 0x100000 * i for i in range(12)]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_header_symbol():
+    names = header_functions()
+    assert set(names) == set(gdn.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (gdn_\w+)", out))
+    missing = set(names) - exported
+    assert not missing, f"declared in gdn.h but not exported: {missing}"
+    lib = ctypes.CDLL(gdn.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_status_strings():
+    assert gdn.gdn_abi_version() == 1
+    seen = set()
+    for code in range(0, 8):
+        s = gdn.gdn_status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 8
+    assert gdn.gdn_status_string(99) == "unknown status"
+
+
+def base_cfg(**kw):
+    c = gdn.gdn_default_config()
+    c.num_seqs, c.tokens_per_seq, c.num_tokens = 4, 1, 4
+    c.num_k_heads, c.num_v_heads, c.head_k_dim, c.head_v_dim = 2, 4, 128, 128
+    c.num_slots = 8
+    c.act_dtype = gdn.GDN_DTYPE_BF16
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def validate(cfg, ptrs=None, cu=None, inter=None):
+    p = list(A[:11]) if ptrs is None else ptrs
+    lib = gdn.raw_library()
+    return lib.gdn_validate(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], cu, p[10],
+                            inter, ctypes.byref(cfg))
+
+
+def test_defaults():
+    c = gdn.gdn_default_config()
+    assert c.tokens_per_seq == 1 and c.scale == 0.0 and abs(c.l2norm_eps - 1e-6) < 1e-12
+    assert c.q_stride_tok == 0 and c.block_v == 0 and c.waves_per_group == 0 and c.flags == 0
+
+
+def test_valid_config_passes():
+    assert validate(base_cfg()) == gdn.GDN_OK
+    assert gdn.gdn_last_error_message() == ""
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_seqs", -1, 2),
+    ("num_k_heads", 0, 2),
+    ("num_v_heads", 3, 2),          # not a multiple of H_k = 2
+    ("head_k_dim", 96, 3),
+    ("head_v_dim", 48, 3),
+    ("head_k_dim", 512, 3),
+    ("act_dtype", 2, 4),
+    ("tokens_per_seq", 0, 2),
+    ("num_tokens", 3, 2),           # < B*T
+    ("num_slots", 0, 2),
+    ("l2norm_eps", -1.0, 7),
+    ("scale", float("nan"), 7),
+    ("q_stride_tok", 100, 2),       # below dense 2*128
+    ("k_stride_tok", 260, 5),       # not a multiple of 8
+    ("v_stride_tok", 516, 5),
+    ("block_v", 12, 7),
+    ("block_v", 256, 7),
+    ("waves_per_group", 9, 7),
+    ("waves_per_group", 3, 7),      # does not divide G*V/BV = 8
+])
+def test_invalid_config(field, value, code):
+    c = base_cfg(**{field: value})
+    assert validate(c) == code
+    assert gdn.gdn_last_error_message() != ""
+
+
+def test_unsupported_block_for_k():
+    # K = 256 with 64-column tiles would need 256 state VGPRs per lane
+    assert validate(base_cfg(head_k_dim=256, block_v=64)) == 7
+
+
+def test_null_pointers():
+    for i in [0, 1, 2, 3, 4, 5, 6, 7, 8, 10]:
+        p = list(A[:11])
+        p[i] = None
+        assert validate(base_cfg(), ptrs=p) == 1, f"pointer {i}"
+
+
+def test_empty_batch_accepts_null_pointers():
+    c = base_cfg(num_seqs=0, num_tokens=0)
+    assert validate(c, ptrs=[None] * 11) == gdn.GDN_OK
+
+
+def test_misaligned_pointers():
+    for i in [0, 1, 2, 7, 10]:
+        p = list(A[:11])
+        p[i] += 8
+        assert validate(base_cfg(), ptrs=p) == 5, f"pointer {i}"
+    p = list(A[:11])
+    p[3] += 1  # a: bf16 needs 2-byte alignment
+    assert validate(base_cfg(), ptrs=p) == 5
+    p = list(A[:11])
+    p[3] += 2  # fine for bf16
+    assert validate(base_cfg(), ptrs=p) == 0
+    assert validate(base_cfg(act_dtype=gdn.GDN_DTYPE_F32), ptrs=p) == 5
+    assert validate(base_cfg(), inter=A[11] + 4) == 5
+
+
+def test_varlen_ignores_tokens_per_seq():
+    c = base_cfg(tokens_per_seq=0, num_tokens=37)
+    assert validate(c, cu=A[9]) == 0
+    assert validate(c) == 2
+
+
+def test_plan_tile_table():
+    decode = gdn.gdn_plan(base_cfg(num_seqs=512, num_tokens=512, num_k_heads=16, num_v_heads=32,
+                                   num_slots=4096), False)
+    assert decode.multi_token == 0 and decode.tokens_per_chunk == 1
+    assert decode.block_v == 32
+    assert decode.waves_per_group == 8 and decode.threads_per_group == 512
+    assert decode.workgroups == 512 * 16          # one per (sequence, k-head)
+    assert decode.lds_bytes == 2 * 128 * 4
+    spec = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
+                                 num_slots=1024), True)
+    assert spec.multi_token == 1 and spec.tokens_per_chunk >= 2
+    multi = gdn.gdn_plan(base_cfg(tokens_per_seq=4, num_tokens=16), False)
+    assert multi.multi_token == 1
+    # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
+    odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32), False)
+    assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
+    forced = gdn.gdn_plan(base_cfg(block_v=16, waves_per_group=4), False)
+    assert forced.block_v == 16 and forced.waves_per_group == 4
+    assert forced.workgroups == 4 * 2 * (2 * 8 // 4)
+
+
+def test_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    q = torch.zeros(2, 1, 32)
+    v = torch.zeros(2, 2, 32)
+    ab = torch.zeros(2, 2)
+    pars = torch.zeros(2)
+    pool = torch.zeros(4, 2, 32, 32)
+    idx = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        gdn.gdn_gating_delta_rule_update(q, q, v, ab, ab, pars, pars, pool, idx)
+    with pytest.raises(ValueError, match="state_idx"):
+        gdn.gdn_gating_delta_rule_update(q, q, v, ab, ab, pars, pars, pool, idx.long())
+    with pytest.raises(TypeError):
+        gdn.gdn_gating_delta_rule_update(q, q, v.double(), ab, ab, pars, pars, pool, idx)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "libgdn.so"))
+    with pytest.raises(ImportError, match="not built"):
+        gdn._load()

@@ -1,0 +1,301 @@
+"""HIP path against the CPU oracle, element by element, on seeded inputs.
+
+Small cases run the oracle on everything and span several wavefront tiles,
+GQA groups, K != V, chunk boundaries of the token loop and ragged tails.  The
+five named workloads run at their full sizes in the launch configuration the
+benchmark times; where the oracle would be slow it checks a sample of
+sequences one by one, and properties (untouched slots, padded rows) are
+checked over everything."""
+import numpy as np
+import pytest
+
+from gpu_helpers import (TOL_STATE_GUARD, announce, live_rows, oracle_on_seqs, rel_err, run_gpu,
+                         to_np, tol_for)
+from linear_attention_recurrent_gating_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def full_check(wl, dev, block_v=0, waves=0, check_inter=True):
+    """Whole-batch parity: out, final states, intermediates, untouched rows."""
+    import torch
+    announce(f"{wl.name} B={wl.num_seqs} H={wl.num_k_heads}/{wl.num_v_heads} K={wl.head_k_dim} "
+             f"V={wl.head_v_dim} act={wl.act} bv={block_v} waves={waves}")
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    pool = torch.from_numpy(pool_np).to(dev)
+    out, inter = run_gpu(inp, pool, dev, block_v=block_v, waves_per_group=waves)
+    seqs = np.arange(wl.num_seqs)
+    ref_pool_rows = pool_np[np.maximum(inp.state_idx, 0)]
+    o_ref, s_ref, i_ref, rows = oracle_on_seqs(inp, ref_pool_rows, seqs,
+                                               intermediates=wl.intermediates)
+    tol = tol_for(wl)
+    live, dead = live_rows(inp)
+    out_np = to_np(out)
+    e_out = rel_err(out_np[live], o_ref[live])
+    assert e_out <= tol, f"out error {e_out:.3e} > {tol}"
+    assert np.all(np.isnan(out_np[dead])), "padded sequences wrote outputs"
+    pool_after = pool.cpu().numpy()
+    lv = inp.state_idx >= 0
+    e_state = rel_err(pool_after[inp.state_idx[lv]], s_ref[lv])
+    assert e_state <= min(tol, TOL_STATE_GUARD), f"state error {e_state:.3e}"
+    untouched = np.setdiff1d(np.arange(wl.num_slots), inp.state_idx[lv])
+    assert np.array_equal(pool_after[untouched], pool_np[untouched]), "untouched slots changed"
+    if wl.intermediates and check_inter:
+        inter_np = inter.cpu().numpy()
+        e_inter = rel_err(inter_np[live], i_ref[live])
+        assert e_inter <= min(tol, TOL_STATE_GUARD), f"intermediate error {e_inter:.3e}"
+        assert np.all(np.isnan(inter_np[dead])), "padded sequences wrote intermediates"
+        # the last token's intermediate is the final state, bitwise
+        ends = np.cumsum(inp.lengths) - 1
+        for i in np.nonzero(lv & (inp.lengths > 0))[0]:
+            assert np.array_equal(inter_np[ends[i]], pool_after[inp.state_idx[i]])
+    return e_out, e_state
+
+
+SMALL = [
+    W.Workload("k32v32_g2_f32_b5", 21, 5, 1, 2, 4, 32, 32, W.ACT_F32, 9, 0.1),
+    W.Workload("k64v64_g2_bf16_b7", 22, 7, 1, 2, 4, 64, 64, W.ACT_BF16, 12, 0.1),
+    W.Workload("k128v128_g2_bf16_b9", 23, 9, 1, 4, 8, 128, 128, W.ACT_BF16, 16, 0.05),
+    W.Workload("k128v128_g2_f32_b9", 24, 9, 1, 4, 8, 128, 128, W.ACT_F32, 16, 0.05),
+    W.Workload("k32v64_g1_f32_t3", 25, 4, 3, 3, 3, 32, 64, W.ACT_F32, 6, 0.1),
+    W.Workload("k64v128_g4_bf16_t2", 26, 3, 2, 1, 4, 64, 128, W.ACT_BF16, 5, 0.1),
+    W.Workload("k256v128_g2_bf16_b3", 27, 3, 1, 2, 4, 256, 128, W.ACT_BF16, 4, 0.05),
+    W.Workload("k128v256_g2_f32_b3", 28, 3, 1, 1, 2, 128, 256, W.ACT_F32, 4, 0.05),
+    W.Workload("k128v128_g3_bf16_b4", 29, 4, 1, 2, 6, 128, 128, W.ACT_BF16, 6, 0.05),
+    W.Workload("k128v128_f32_t17_inter", 30, 3, 17, 2, 4, 128, 128, W.ACT_F32, 5, 0.05,
+               intermediates=True),
+    W.Workload("varlen_0_40_bf16", 31, 6, 1, 2, 4, 128, 128, W.ACT_BF16, 8, 0.05, varlen=True,
+               len_range=(0, 40)),
+    W.Workload("varlen_pad_inter_f32", 32, 9, 1, 2, 4, 64, 64, W.ACT_F32, 12, 0.1, varlen=True,
+               len_range=(1, 20), num_padded=3, intermediates=True),
+    W.Workload("k128v128_weak_decay_t9", 33, 4, 9, 2, 4, 128, 128, W.ACT_F32, 5, 0.05,
+               decay="weak"),
+    W.Workload("tiny_fp32_weak_decay", 0, 2, 1, 2, 4, 32, 32, W.ACT_F32, 4, 0.1,
+               fixed_slots=(2, 0), decay="weak"),
+]
+
+
+def test_tiny_fp32(dev):
+    full_check(W.TINY_F32, dev)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_small(dev, wl):
+    full_check(wl, dev)
+
+
+@pytest.mark.parametrize("t", [1, 5, 20])
+def test_tile_overrides(dev, t):
+    """Every tile width and workgroup size of the table on one shape."""
+    for bv in (8, 16, 32, 64):
+        for waves in (1, 2, 4, 8):
+            units = 2 * (128 // bv)
+            if units % waves:
+                continue
+            wl = W.Workload(f"override_t{t}", 40 + t, 3, t, 2, 4, 128, 128, W.ACT_F32, 5, 0.05,
+                            intermediates=(t == 5))
+            full_check(wl, dev, block_v=bv, waves=waves)
+
+
+def test_qwen3next_b64(dev):
+    full_check(W.QWEN3NEXT_B64, dev)
+
+
+def test_spec_verify_b128_t4(dev):
+    full_check(W.SPEC_VERIFY, dev)
+
+
+def test_spec_verify_weak_decay(dev):
+    full_check(W.SPEC_VERIFY.with_(name="spec_verify_weak", decay="weak", seed=44), dev)
+
+
+def test_varlen_long(dev):
+    full_check(W.VARLEN_LONG, dev)
+
+
+def test_varlen_long_weak_decay(dev):
+    full_check(W.VARLEN_LONG.with_(name="varlen_long_weak", decay="weak", seed=45), dev)
+
+
+@pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
+def test_decode_b512_full_size_sampled(dev, wl):
+    """Full-size decode in the benchmark's launch configuration; the oracle
+    checks 48 sampled sequences (every v-head), the untouched slots are
+    checked bitwise over the whole 4096-slot pool."""
+    import torch
+    announce(f"{wl.name} full size")
+    inp = W.make_host_inputs(wl)
+    pool = W.make_pool_torch(wl, dev)
+    pool0 = pool.clone()
+    out, _ = run_gpu(inp, pool, dev)
+    rng = np.random.default_rng(99)
+    seqs = np.sort(rng.choice(wl.num_seqs, size=48, replace=False))
+    slots = inp.state_idx[seqs]
+    o_ref, s_ref, _, rows = oracle_on_seqs(inp, pool0[torch.from_numpy(slots).long().to(dev)].cpu().numpy(),
+                                           seqs)
+    e_out = rel_err(to_np(out[torch.from_numpy(rows).to(dev)]), o_ref)
+    assert e_out <= tol_for(wl), f"out error {e_out:.3e}"
+    got = pool[torch.from_numpy(slots).long().to(dev)].cpu().numpy()
+    e_state = rel_err(got, s_ref)
+    assert e_state <= TOL_STATE_GUARD, f"state error {e_state:.3e}"
+    changed = (pool != pool0).flatten(1).any(dim=1).cpu().numpy()
+    assert set(np.nonzero(changed)[0]) <= set(inp.state_idx.tolist()), "untouched slot changed"
+    assert not torch.isnan(out).any(), "an output row was not written"
+
+
+def test_chain_equals_multi_token_bitwise(dev):
+    """A T-token call equals T chained one-token calls bit for bit (same fp32
+    state both ways), and each chained state equals the intermediate."""
+    import torch
+    announce("chain bitwise")
+    wl = W.Workload("chain", 50, 3, 6, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05, intermediates=True)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    pool_multi = torch.from_numpy(pool_np).to(dev)
+    out_multi, inter = run_gpu(inp, pool_multi, dev)
+    pool_chain = torch.from_numpy(pool_np).to(dev)
+    T = wl.tokens_per_seq
+    for t in range(T):
+        rows = np.arange(wl.num_seqs) * T + t
+        step = W.HostInputs(wl.with_(tokens_per_seq=1, intermediates=False), inp.q[rows],
+                            inp.k[rows], inp.v[rows], inp.a[rows], inp.b[rows], inp.A_log,
+                            inp.dt_bias, inp.state_idx, None, np.ones(wl.num_seqs, np.int64),
+                            {n: x[rows] for n, x in inp.bits.items()})
+        out_t, _ = run_gpu(step, pool_chain, dev)
+        assert torch.equal(out_t, out_multi[torch.from_numpy(rows).to(dev)]), f"out differs at t={t}"
+        for i in range(wl.num_seqs):
+            assert torch.equal(pool_chain[int(inp.state_idx[i])], inter[int(rows[i])]), \
+                f"state differs at t={t}, seq {i}"
+    assert torch.equal(pool_chain, pool_multi)
+
+
+def test_deterministic(dev):
+    import torch
+    announce("determinism")
+    wl = W.VARLEN_LONG.with_(name="det", num_seqs=3, len_range=(20, 70), seed=51)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    p1 = torch.from_numpy(pool_np).to(dev)
+    p2 = torch.from_numpy(pool_np).to(dev)
+    o1, _ = run_gpu(inp, p1, dev)
+    o2, _ = run_gpu(inp, p2, dev)
+    assert torch.equal(o1.nan_to_num(), o2.nan_to_num()) and torch.equal(p1, p2)
+
+
+def test_strided_views_match_dense(dev):
+    """q/k/v as column slices of one fused projection (token stride larger
+    than the dense row) give the dense result bit for bit."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce("strided views")
+    wl = W.Workload("strided", 52, 6, 3, 2, 4, 128, 128, W.ACT_BF16, 8, 0.05)
+    inp = W.make_host_inputs(wl)
+    d = W.to_torch(inp, dev)
+    pool_np = W.make_pool_host(wl)
+    p_dense = torch.from_numpy(pool_np).to(dev)
+    o_dense, _ = run_gpu(inp, p_dense, dev, tensors=d)
+    N = inp.num_tokens
+    Hk, Hv, K, V = 2, 4, 128, 128
+    width = 2 * Hk * K + Hv * V + 64           # padding keeps the stride a multiple of 8
+    fused = torch.zeros(N, width, dtype=torch.bfloat16, device=dev)
+    fused[:, :Hk * K] = d["q"].reshape(N, -1)
+    fused[:, Hk * K:2 * Hk * K] = d["k"].reshape(N, -1)
+    fused[:, 2 * Hk * K:2 * Hk * K + Hv * V] = d["v"].reshape(N, -1)
+    q = fused[:, :Hk * K].view(N, Hk, K)
+    k = fused[:, Hk * K:2 * Hk * K].view(N, Hk, K)
+    v = fused[:, 2 * Hk * K:2 * Hk * K + Hv * V].view(N, Hv, V)
+    assert q.stride(0) == width
+    p_str = torch.from_numpy(pool_np).to(dev)
+    out = torch.empty(N, Hv, V, dtype=torch.bfloat16, device=dev)
+    gdn.gdn_gating_delta_rule_update(q, k, v, d["a"], d["b"], d["A_log"], d["dt_bias"], p_str,
+                                     d["state_idx"], None, out, tokens_per_seq=3)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_dense) and torch.equal(p_str, p_dense)
+
+
+def test_no_final_writeback(dev):
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce("no final writeback")
+    wl = W.SPEC_VERIFY.with_(name="nfw", num_seqs=10, num_padded=2, num_slots=16, seed=53)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    p1 = torch.from_numpy(pool_np).to(dev)
+    o1, i1 = run_gpu(inp, p1, dev)
+    p2 = torch.from_numpy(pool_np).to(dev)
+    o2, i2 = run_gpu(inp, p2, dev, flags=gdn.GDN_FLAG_NO_FINAL_WRITEBACK)
+    assert torch.equal(p2.cpu(), torch.from_numpy(pool_np)), "pool changed"
+    assert torch.equal(o1.nan_to_num(), o2.nan_to_num()) and torch.equal(i1.nan_to_num(), i2.nan_to_num())
+
+
+def test_debug_checks_reject_contract_violations(dev):
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce("debug checks")
+    wl = W.Workload("dbg", 54, 4, 1, 2, 4, 64, 64, W.ACT_F32, 6, 0.1)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    pool = torch.from_numpy(pool_np).to(dev)
+    d = W.to_torch(inp, dev)
+    ok, _ = run_gpu(inp, pool.clone(), dev, tensors=d, flags=gdn.GDN_FLAG_DEBUG_CHECKS)
+    dup = d["state_idx"].clone()
+    dup[1] = dup[0]
+    big = d["state_idx"].clone()
+    big[2] = wl.num_slots
+    for bad in (dup, big):
+        dd = dict(d, state_idx=bad)
+        with pytest.raises(gdn.GdnError) as ei:
+            run_gpu(inp, pool, dev, tensors=dd, flags=gdn.GDN_FLAG_DEBUG_CHECKS)
+        assert ei.value.status == 7
+    assert torch.equal(pool.cpu(), torch.from_numpy(pool_np)), "a rejected call launched"
+    wlv = W.Workload("dbgv", 55, 3, 1, 2, 4, 64, 64, W.ACT_F32, 6, 0.1, varlen=True,
+                     len_range=(1, 3))
+    inpv = W.make_host_inputs(wlv)
+    dv = W.to_torch(inpv, dev)
+    cu_bad = dv["cu_seqlens"].clone()
+    cu_bad[1], cu_bad[2] = cu_bad[2], cu_bad[1]
+    if cu_bad[1] != cu_bad[2]:
+        with pytest.raises(gdn.GdnError):
+            run_gpu(inpv, pool, dev, tensors=dict(dv, cu_seqlens=cu_bad),
+                    flags=gdn.GDN_FLAG_DEBUG_CHECKS)
+
+
+def test_empty_batch_launches_nothing(dev):
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    z = torch.zeros(0, 2, 64, device=dev)
+    zv = torch.zeros(0, 4, 64, device=dev)
+    zab = torch.zeros(0, 4, device=dev)
+    par = torch.zeros(4, device=dev)
+    pool = torch.ones(3, 4, 64, 64, device=dev)
+    idx = torch.zeros(0, dtype=torch.int32, device=dev)
+    gdn.gdn_gating_delta_rule_update(z, z, zv, zab, zab, par, par, pool, idx, tokens_per_seq=1)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, torch.ones_like(pool))
+
+
+def test_side_stream(dev):
+    """The call runs on the stream it is given."""
+    import torch
+    announce("side stream")
+    wl = W.Workload("stream", 56, 4, 2, 2, 4, 128, 128, W.ACT_BF16, 6, 0.05)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    p1 = torch.from_numpy(pool_np).to(dev)
+    o1, _ = run_gpu(inp, p1, dev)
+    p2 = torch.from_numpy(pool_np).to(dev)
+    d = W.to_torch(inp, dev)
+    s = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o2, _ = run_gpu(inp, p2, dev, tensors=d, stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(p1, p2)
