@@ -1,0 +1,226 @@
+"""Throughput of the fused gating + gated delta-rule decode update on one GPU.
+
+A step is one call of the update over one batch: by default the bs=512
+decode of Qwen3-Next-shaped heads (H_k=16, H_v=32, K=V=128, bf16
+activations, fp32 state in a 4096-slot pool).  Every step uses the next of 8
+disjoint 512-slot sets, so each step's 1 GiB of state is read from HBM rather
+than from the 256 MB Infinity Cache.
+
+Prints one JSON line: updates/s (one update = one (sequence, v-head, token)
+step of a live sequence), the kernel's HBM roofline fraction from HIP events
+on the launch stream, the counter-measured traffic when the kernel source
+still matches the committed counter profile, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linear_attention_recurrent_gating_amd import workloads as W  # noqa: E402
+
+METRIC = "state updates/sec (seq·head·token) + HBM GB/s as % of peak, bs=512 decode"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc", "gdn_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """Counter-measured HBM bytes per launch from the committed profile, or
+    None when there is none or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"gdn_fused_update_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(inp, pool_rows: np.ndarray, budget_s: float):
+    """The oracle on the same batch (its own copy of the gathered states),
+    repeated until about `budget_s` seconds have passed."""
+    import oracle
+    threads = cpu_threads()
+    B = inp.wl.num_seqs
+    idx = np.where(inp.state_idx >= 0, np.arange(B), -1).astype(np.int32)
+    pool = np.ascontiguousarray(pool_rows, dtype=np.float32).copy()
+    oracle.build(force=False)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.update(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias, pool, idx,
+                      inp.cu_seqlens, tokens_per_seq=inp.wl.tokens_per_seq, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    updates = W.active_updates(inp) * reps
+    return {"value": updates / el, "unit": "updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {inp.wl.name} batch ({B} sequences x {inp.wl.num_v_heads} "
+                      f"v-heads), fp64 oracle, repeated {reps}x over {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=W.DECODE_B512.name, choices=sorted(W.ALL))
+    ap.add_argument("--slot-sets", type=int, default=8)
+    ap.add_argument("--block-v", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for the CPU baseline (0 skips it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead: time a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the update shards by sequence or head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                          "launches": args.warmup + args.steps, "copy_gb_s": 8 * n / el / 1e9}))
+        return
+
+    wl = W.ALL[args.workload]
+    inp = W.make_host_inputs(wl)
+    d = W.to_torch(inp, dev)
+    sets = max(1, args.slot_sets if wl.num_slots >= args.slot_sets * wl.num_seqs else 1)
+    # Disjoint slot sets: set s maps sequence i to slot s*B + i of a permuted pool.
+    B = wl.num_seqs
+    live = inp.state_idx >= 0
+    idx_sets = []
+    rng = np.random.default_rng(wl.seed + 7)
+    perm = rng.permutation(wl.num_slots)
+    for s in range(sets):
+        idx = perm[s * B:(s + 1) * B].astype(np.int32) if sets > 1 else inp.state_idx.copy()
+        idx[~live] = -1
+        idx_sets.append(torch.from_numpy(idx).to(dev))
+    pool = W.make_pool_torch(wl, dev)
+    act = torch.bfloat16 if wl.act == W.ACT_BF16 else torch.float32
+    out = torch.empty(inp.num_tokens, wl.num_v_heads, wl.head_v_dim, dtype=act, device=dev)
+    inter = None
+    if wl.intermediates:
+        inter = torch.empty(inp.num_tokens, wl.num_v_heads, wl.head_k_dim, wl.head_v_dim,
+                            dtype=torch.float32, device=dev)
+    # the oracle's copy of the first set's initial states, taken before any update
+    pool_rows0 = None
+    if args.cpu_budget > 0:
+        pool_rows0 = pool[idx_sets[0].clamp(min=0).long()].cpu().numpy()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gdn.gdn_gating_delta_rule_update(
+            d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool,
+            idx_sets[i % sets], d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
+            block_v=args.block_v, waves_per_group=args.waves, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    updates = W.active_updates(inp)
+    alg_bytes = W.algorithmic_bytes(inp)
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    value = updates * args.steps / wall
+    info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
+                                        tokens_per_seq=wl.tokens_per_seq, block_v=args.block_v,
+                                        waves_per_group=args.waves), d["cu_seqlens"] is not None)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": B, "tokens": inp.num_tokens,
+                   "num_k_heads": wl.num_k_heads, "num_v_heads": wl.num_v_heads,
+                   "head_k_dim": wl.head_k_dim, "head_v_dim": wl.head_v_dim,
+                   "activations": wl.act, "state": "f32", "pool_slots": wl.num_slots,
+                   "slot_sets": sets, "block_v": info.block_v,
+                   "waves_per_group": info.waves_per_group, "workgroups": info.workgroups,
+                   "parallelism": "single GPU"},
+        "hbm_gb_s": achieved,
+        "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
+        "kernel_us": kern_ms * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(wl.name),
+                     "algorithmic_bytes": alg_bytes, "kernel": "gdn_fused_update"},
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, pool_rows0, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -95,14 +95,24 @@ typedef struct gdn_config {
     int64_t k_stride_tok;    /* same for k                                       */
     int64_t v_stride_tok;    /* same for v (dense = H_v*V)                       */
     uint32_t flags;          /* GDN_FLAG_*                                       */
-    int32_t block_v;         /* V-columns per wavefront tile: 0 = library choice,
-                                else 8, 16, 32 or 64 (dividing V)                */
-    int32_t waves_per_group; /* wavefronts per workgroup: 0 = library choice,
-                                else 1..8, dividing G*V/block_v                  */
+    int32_t block_v;         /* 0 = library choice (row-split kernel for one token
+                                per sequence, 32-column tiles otherwise); else
+                                force the column-tile kernel with 8, 16, 32 or
+                                64 columns per wavefront (dividing V)            */
+    int32_t waves_per_group; /* 0 = library choice; else force the column-tile
+                                kernel with 1..8 wavefronts per workgroup,
+                                dividing G*V/block_v                             */
 } gdn_config;
+
+/* Kernel families (gdn_launch_info.kernel_family). */
+#define GDN_KERNEL_COLUMN_TILES 0 /* wavefront = (v-head, block_v columns, all K
+                                     rows); any number of tokens               */
+#define GDN_KERNEL_ROW_SPLIT 1    /* wavefront = (v-head, all V columns, a block
+                                     of K rows); single-token decode           */
 
 /* Describes the launch that a configuration maps to (gdn_plan). */
 typedef struct gdn_launch_info {
+    int32_t kernel_family;    /* GDN_KERNEL_*                                */
     int32_t block_v;          /* V-columns per wavefront                     */
     int32_t waves_per_group;  /* wavefronts per workgroup                    */
     int32_t tokens_per_chunk; /* tokens staged in LDS at a time              */

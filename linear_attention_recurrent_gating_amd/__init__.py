@@ -22,6 +22,8 @@ GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 GDN_FLAG_NO_FINAL_WRITEBACK = 0x1
 GDN_FLAG_DEBUG_CHECKS = 0x2
+GDN_KERNEL_COLUMN_TILES = 0
+GDN_KERNEL_ROW_SPLIT = 1
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
                 3: "GDN_ERR_UNSUPPORTED_SHAPE", 4: "GDN_ERR_UNSUPPORTED_DTYPE",
@@ -45,7 +47,8 @@ class GdnConfig(ctypes.Structure):
 
 
 class GdnLaunchInfo(ctypes.Structure):
-    _fields_ = [("block_v", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
+    _fields_ = [("kernel_family", ctypes.c_int32), ("block_v", ctypes.c_int32),
+                ("waves_per_group", ctypes.c_int32),
                 ("tokens_per_chunk", ctypes.c_int32), ("multi_token", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("threads_per_group", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32)]

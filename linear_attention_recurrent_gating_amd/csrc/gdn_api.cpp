@@ -116,17 +116,32 @@ gdn_status check_config(const gdn_config* cfg, bool has_cu) {
     return GDN_OK;
 }
 
+// Single-token calls without a tiling override use the row-split kernel
+// (contiguous kilobyte per load/store instruction); everything else uses the
+// column-tile kernel.
 void make_shape(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
     const int G = c.num_v_heads / c.num_k_heads;
     s.K = c.head_k_dim;
-    s.block_v = c.block_v ? c.block_v : default_block_v(c);
     s.act = c.act_dtype;
     s.multi_token = (has_cu || c.tokens_per_seq > 1) ? 1 : 0;
-    const int units = G * (c.head_v_dim / s.block_v);
-    s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
     s.chunk = s.multi_token ? gdn::kChunkTokens : 1;
-    s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
-    s.lds_bytes = gdn::lds_bytes_for(s.K, s.block_v, s.waves, s.chunk, s.multi_token);
+    const int kw = gdn::rows_waves_per_head(c.head_k_dim, c.head_v_dim);
+    if (!s.multi_token && c.block_v == 0 && c.waves_per_group == 0 && kw > 0) {
+        s.kind = gdn::kKindRows;
+        s.block_v = c.head_v_dim;
+        int heads = 1;  // v-heads per workgroup: largest divisor of G within 8 waves
+        for (int hp = G; hp >= 1; --hp)
+            if (G % hp == 0 && hp * kw <= 8) { heads = hp; break; }
+        s.waves = heads * kw;
+        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (G / heads);
+    } else {
+        s.kind = gdn::kKindColumns;
+        s.block_v = c.block_v ? c.block_v : default_block_v(c);
+        const int units = G * (c.head_v_dim / s.block_v);
+        s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
+    }
+    s.lds_bytes = gdn::lds_bytes_for(s, c.head_v_dim);
 }
 
 gdn_status debug_check_indices(const gdn_config& c, const int32_t* state_idx,
@@ -208,6 +223,7 @@ gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* 
     if (s != GDN_OK) return s;
     gdn::LaunchShape sh{};
     make_shape(*cfg, has_cu_seqlens != 0, sh);
+    info->kernel_family = sh.kind;
     info->block_v = sh.block_v;
     info->waves_per_group = sh.waves;
     info->tokens_per_chunk = sh.chunk;
@@ -260,7 +276,7 @@ gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void
     p.Hv = c.num_v_heads;
     p.G = c.num_v_heads / c.num_k_heads;
     p.V = c.head_v_dim;
-    p.groups_per_khead = (p.G * (c.head_v_dim / sh.block_v)) / sh.waves;
+    p.groups_per_khead = static_cast<int32_t>(sh.groups / (static_cast<int64_t>(c.num_seqs) * c.num_k_heads));
     p.scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt(static_cast<float>(c.head_k_dim));
     p.eps = c.l2norm_eps;
     p.write_final = (c.flags & GDN_FLAG_NO_FINAL_WRITEBACK) ? 0 : 1;
@@ -271,9 +287,10 @@ gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void
     }();
     if (log)
         std::fprintf(stderr,
-                     "[gdn] K=%d V=%d act=%s multi_token=%d block_v=%d waves=%d chunk=%d groups=%lld "
-                     "lds=%d\n",
-                     sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", sh.multi_token, sh.block_v,
+                     "[gdn] %s K=%d V=%d act=%s multi_token=%d block_v=%d waves=%d chunk=%d "
+                     "groups=%lld lds=%d\n",
+                     sh.kind == gdn::kKindRows ? "rows" : "columns", sh.K, c.head_v_dim,
+                     sh.act ? "bf16" : "f32", sh.multi_token, sh.block_v,
                      sh.waves, sh.chunk, static_cast<long long>(sh.groups), sh.lds_bytes);
 
     const hipError_t e = gdn::launch_fused(sh, p, st);

@@ -36,7 +36,12 @@ struct FusedParams {
     int32_t write_final;        // 0 under GDN_FLAG_NO_FINAL_WRITEBACK
 };
 
+// Kernel families.
+constexpr int kKindColumns = 0;  // wave = (v-head, BV-column tile); any token count
+constexpr int kKindRows = 1;     // wave = (v-head, block of whole rows); one token
+
 struct LaunchShape {
+    int kind;
     int K;
     int block_v;
     int act;          // 0 = fp32, 1 = bf16
@@ -50,11 +55,15 @@ struct LaunchShape {
 // Tokens staged in LDS at a time by the multi-token kernel.
 constexpr int kChunkTokens = 16;
 
-// Dynamic LDS bytes of a launch shape.
-int lds_bytes_for(int K, int block_v, int waves, int chunk, int multi_token);
+// Dynamic LDS bytes of a launch shape (V = head_v_dim).
+int lds_bytes_for(const LaunchShape& shape, int V);
 
-// True when a kernel instance exists for (K, block_v).
+// True when a column-tile kernel instance exists for (K, block_v).
 bool instance_exists(int K, int block_v);
+
+// Wavefronts per v-head of the row-split kernel for (K, V); 0 if it has no
+// instance for that pair.
+int rows_waves_per_head(int K, int V);
 
 // Enqueues the fused kernel; returns the HIP launch status.
 hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);

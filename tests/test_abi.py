@@ -146,19 +146,29 @@ def test_plan_tile_table():
     decode = gdn.gdn_plan(base_cfg(num_seqs=512, num_tokens=512, num_k_heads=16, num_v_heads=32,
                                    num_slots=4096), False)
     assert decode.multi_token == 0 and decode.tokens_per_chunk == 1
-    assert decode.block_v == 32
+    assert decode.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
+    assert decode.block_v == 128                   # whole rows per wavefront
     assert decode.waves_per_group == 8 and decode.threads_per_group == 512
     assert decode.workgroups == 512 * 16          # one per (sequence, k-head)
-    assert decode.lds_bytes == 2 * 128 * 4
+    assert decode.lds_bytes == (2 * 128 + 8 * (2 * 128 + 4)) * 4
+    # K = V = 256 would need 16 row blocks per head: the column-tile kernel takes it
+    big = gdn.gdn_plan(base_cfg(head_k_dim=256, head_v_dim=256), False)
+    assert big.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and big.block_v == 32
     spec = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
                                  num_slots=1024), True)
     assert spec.multi_token == 1 and spec.tokens_per_chunk >= 2
+    assert spec.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and spec.block_v == 32
     multi = gdn.gdn_plan(base_cfg(tokens_per_seq=4, num_tokens=16), False)
     assert multi.multi_token == 1
     # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
-    odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32), False)
+    odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32), True)
     assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
+    # row split with G = 3, K = V = 128: 4 waves per head, one head per group
+    odd_rows = gdn.gdn_plan(base_cfg(num_v_heads=6), False)
+    assert odd_rows.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
+    assert odd_rows.waves_per_group == 4 and odd_rows.workgroups == 4 * 2 * 3
     forced = gdn.gdn_plan(base_cfg(block_v=16, waves_per_group=4), False)
+    assert forced.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
     assert forced.block_v == 16 and forced.waves_per_group == 4
     assert forced.workgroups == 4 * 2 * (2 * 8 // 4)
 

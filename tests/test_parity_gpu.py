@@ -87,6 +87,35 @@ def test_tiny_fp32(dev):
     full_check(W.TINY_F32, dev)
 
 
+ROW_SPLIT_PAIRS = [(K, V) for K in (32, 64, 128, 256) for V in (32, 64, 128, 256)]
+
+
+@pytest.mark.parametrize("K,V", ROW_SPLIT_PAIRS, ids=lambda x: str(x))
+def test_single_token_all_head_dims(dev, K, V):
+    """Single-token decode over every supported (K, V): the row-split kernel
+    (column tiles for K = V = 256), bf16 and fp32."""
+    for act, seed in ((W.ACT_BF16, 60), (W.ACT_F32, 61)):
+        wl = W.Workload(f"decode_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
+                        num_padded=1)
+        full_check(wl, dev)
+
+
+def test_decode_kernel_families_agree(dev):
+    """The row-split and column-tile single-token kernels differ only in the
+    order of their fp32 reductions."""
+    import torch
+    announce("decode kernel families")
+    wl = W.Workload("families", 62, 16, 1, 4, 8, 128, 128, W.ACT_F32, 20, 0.05)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    p_rows = torch.from_numpy(pool_np).to(dev)
+    p_cols = torch.from_numpy(pool_np).to(dev)
+    o_rows, _ = run_gpu(inp, p_rows, dev)
+    o_cols, _ = run_gpu(inp, p_cols, dev, block_v=32)
+    assert rel_err(to_np(o_rows), to_np(o_cols)) <= 1e-5
+    assert rel_err(p_rows.cpu().numpy(), p_cols.cpu().numpy()) <= 1e-5
+
+
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
 def test_small(dev, wl):
     full_check(wl, dev)
@@ -153,7 +182,10 @@ def test_decode_b512_full_size_sampled(dev, wl):
 
 def test_chain_equals_multi_token_bitwise(dev):
     """A T-token call equals T chained one-token calls bit for bit (same fp32
-    state both ways), and each chained state equals the intermediate."""
+    state both ways), and each chained state equals the intermediate.  The
+    one-token calls pass cu_seqlens so that they run the same (multi-token)
+    kernel family; the row-split decode kernel agrees only to rounding
+    (test_decode_kernel_families_agree, test_chain_through_decode_kernel)."""
     import torch
     announce("chain bitwise")
     wl = W.Workload("chain", 50, 3, 6, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05, intermediates=True)
@@ -165,9 +197,11 @@ def test_chain_equals_multi_token_bitwise(dev):
     T = wl.tokens_per_seq
     for t in range(T):
         rows = np.arange(wl.num_seqs) * T + t
-        step = W.HostInputs(wl.with_(tokens_per_seq=1, intermediates=False), inp.q[rows],
-                            inp.k[rows], inp.v[rows], inp.a[rows], inp.b[rows], inp.A_log,
-                            inp.dt_bias, inp.state_idx, None, np.ones(wl.num_seqs, np.int64),
+        step = W.HostInputs(wl.with_(tokens_per_seq=1, intermediates=False, varlen=True),
+                            inp.q[rows], inp.k[rows], inp.v[rows], inp.a[rows], inp.b[rows],
+                            inp.A_log, inp.dt_bias, inp.state_idx,
+                            np.arange(wl.num_seqs + 1, dtype=np.int32),
+                            np.ones(wl.num_seqs, np.int64),
                             {n: x[rows] for n, x in inp.bits.items()})
         out_t, _ = run_gpu(step, pool_chain, dev)
         assert torch.equal(out_t, out_multi[torch.from_numpy(rows).to(dev)]), f"out differs at t={t}"
@@ -175,6 +209,31 @@ def test_chain_equals_multi_token_bitwise(dev):
             assert torch.equal(pool_chain[int(inp.state_idx[i])], inter[int(rows[i])]), \
                 f"state differs at t={t}, seq {i}"
     assert torch.equal(pool_chain, pool_multi)
+
+
+def test_chain_through_decode_kernel(dev):
+    """T chained single-token decode calls (row-split kernel) follow a T-token
+    call to fp32 rounding, token by token."""
+    import torch
+    announce("chain through decode kernel")
+    wl = W.Workload("chain_rows", 57, 4, 8, 2, 4, 128, 128, W.ACT_F32, 6, 0.05,
+                    intermediates=True)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    pool_multi = torch.from_numpy(pool_np).to(dev)
+    out_multi, inter = run_gpu(inp, pool_multi, dev)
+    pool_chain = torch.from_numpy(pool_np).to(dev)
+    T = wl.tokens_per_seq
+    for t in range(T):
+        rows = np.arange(wl.num_seqs) * T + t
+        step = W.HostInputs(wl.with_(tokens_per_seq=1, intermediates=False), inp.q[rows],
+                            inp.k[rows], inp.v[rows], inp.a[rows], inp.b[rows], inp.A_log,
+                            inp.dt_bias, inp.state_idx, None, np.ones(wl.num_seqs, np.int64), {})
+        out_t, _ = run_gpu(step, pool_chain, dev)
+        r = torch.from_numpy(rows).to(dev)
+        assert rel_err(to_np(out_t), to_np(out_multi[r])) <= 1e-5, f"t={t}"
+        slots = torch.from_numpy(inp.state_idx).long().to(dev)
+        assert rel_err(pool_chain[slots].cpu().numpy(), inter[r].cpu().numpy()) <= 1e-5
 
 
 def test_deterministic(dev):
