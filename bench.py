@@ -34,15 +34,22 @@ KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc",
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+KERNEL_NAMES = {0: "gdn_fused_update", 1: "gdn_decode_rows"}   # by gdn_launch_info.kernel_family
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def counter_traffic(workload: str):
+def profile_path(kernel: str, workload: str, kind: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}__{workload}__{kind}.txt")
+
+
+def counter_traffic(kernel: str, workload: str):
     """Counter-measured HBM bytes per launch from the committed profile, or
     None when there is none or the kernel source changed since."""
-    path = os.path.join(PROFILES, f"gdn_fused_update_{workload}_counters.txt")
+    path = profile_path(kernel, workload, "counters")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -90,6 +97,70 @@ def cpu_baseline(inp, pool_rows: np.ndarray, budget_s: float):
                       f"v-heads), fp64 oracle, repeated {reps}x over {el:.1f} s"}
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict):
+    """Writes the committed text summaries of one workload from rocprofv3 CSV
+    output: the --kernel-trace --stats table, and HBM traffic per launch from
+    the FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same counter
+    reads for a plain 1 GiB device copy (__amd_rocclr_copyBuffer)."""
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = _csv_rows(os.path.join(prof_dir, "trace", "run_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel-trace summary: {kernel}, workload {workload}",
+             f"# command: {commands['trace']}",
+             f"# kernel source sha256[:16] = {kernel_source_hash()}",
+             "# name | calls | average_us | min_us | max_us | percent"]
+    import re
+    for r in stats:
+        m = re.search(r"(gdn_\w+<[^>]*>)", r["Name"])
+        short = m.group(1) if m else r["Name"].replace("void ", "")[:60]
+        lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}")
+    with open(profile_path(kernel, workload, "kernel_trace"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_dispatch(counter, copy):
+        sub = ("copy_" if copy else "") + counter
+        rows = _csv_rows(os.path.join(prof_dir, sub, "run_counter_collection.csv"))
+        want = "__amd_rocclr_copyBuffer" if copy else kernel
+        vals = [float(r["Counter_Value"]) for r in rows
+                if want in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return sum(vals) / len(vals), len(vals)
+
+    gib_kib = (1 << 30) / 1024
+    fetch, nf = per_dispatch("FETCH_SIZE", False)
+    write, nw = per_dispatch("WRITE_SIZE", False)
+    cfetch, _ = per_dispatch("FETCH_SIZE", True)
+    cwrite, _ = per_dispatch("WRITE_SIZE", True)
+    f_fac, w_fac = gib_kib / cfetch, gib_kib / cwrite
+    traffic = (fetch * f_fac + write * w_fac) * 1024
+    wl = W.ALL[workload]
+    alg = W.algorithmic_bytes(W.make_host_inputs(wl))
+    out = [f"# rocprofv3 HBM counters: {kernel}, workload {workload}",
+           f"# command (FETCH_SIZE): {commands['fetch']}",
+           f"# command (WRITE_SIZE): {commands['write']}",
+           f"# calibration: {commands['copy']} (1 GiB read + 1 GiB written per dispatch)",
+           f"# summarised by: {commands['summary']}",
+           f"kernel_source_sha256_16 = {kernel_source_hash()}",
+           f"fetch_kib_per_dispatch = {fetch:.1f}   # mean over {nf} dispatches",
+           f"write_kib_per_dispatch = {write:.1f}   # mean over {nw} dispatches",
+           f"copy_fetch_kib_per_dispatch = {cfetch:.1f}",
+           f"copy_write_kib_per_dispatch = {cwrite:.1f}",
+           f"fetch_calibration_factor = {f_fac:.4f}",
+           f"write_calibration_factor = {w_fac:.4f}",
+           f"traffic_bytes_per_launch = {traffic:.0f}",
+           f"algorithmic_bytes_per_launch = {alg}",
+           f"traffic_over_algorithmic = {traffic / alg:.4f}"]
+    with open(profile_path(kernel, workload, "counters"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(lines + out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,7 +174,29 @@ def main():
                     help="seconds of oracle time for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead: time a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="instead: write profiles/ summaries from rocprofv3 CSV output in DIR "
+                         "(subdirectories trace, FETCH_SIZE, WRITE_SIZE, copy_FETCH_SIZE, "
+                         "copy_WRITE_SIZE)")
+    ap.add_argument("--kernel", default="gdn_decode_rows", help="kernel name for --summarize-profiles")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        d = args.summarize_profiles
+        run = f"python3 bench.py --workload {args.workload}"
+        summarize_profiles(d, args.workload, args.kernel, {
+            "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
+                     f"{run} --steps 50 --warmup 5 --cpu-budget 0",
+            "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE -o run -- "
+                     f"{run} --steps 5 --warmup 1 --cpu-budget 0",
+            "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE -o run -- "
+                     f"{run} --steps 5 --warmup 1 --cpu-budget 0",
+            "copy": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d "
+                    f"{d}/copy_<counter> -o run -- python3 bench.py --copy-calibration --steps 3 "
+                    f"--warmup 1",
+            "summary": f"python3 bench.py --workload {args.workload} --kernel {args.kernel} "
+                       f"--summarize-profiles {d}"})
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -213,8 +306,9 @@ def main():
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,
         "kernel_us": kern_ms * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(wl.name),
-                     "algorithmic_bytes": alg_bytes, "kernel": "gdn_fused_update"},
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(KERNEL_NAMES[info.kernel_family], wl.name),
+                     "algorithmic_bytes": alg_bytes, "kernel": KERNEL_NAMES[info.kernel_family]},
         "cpu_baseline": None,
     }
     if args.cpu_budget > 0:
