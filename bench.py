@@ -34,7 +34,7 @@ KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc",
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNEL_NAMES = {0: "gdn_fused_update", 1: "gdn_decode_rows"}   # by gdn_launch_info.kernel_family
+KERNEL_NAMES = {1: "gdn_fused_update", 2: "gdn_decode_rows", 3: "gdn_vk_update"}  # by kernel_family
 
 
 def kernel_source_hash() -> str:
@@ -168,7 +168,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.DECODE_B512.name, choices=sorted(W.ALL))
     ap.add_argument("--slot-sets", type=int, default=8)
+    ap.add_argument("--family", type=int, default=0,
+                    help="0 auto, 1 column tiles, 2 row split, 3 value rows (VK layout)")
+    ap.add_argument("--layout", default="KV", choices=["KV", "VK"],
+                    help="storage order of the state tiles")
     ap.add_argument("--block-v", type=int, default=0)
+    ap.add_argument("--block-k", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0 skips it)")
@@ -239,16 +244,20 @@ def main():
         idx[~live] = -1
         idx_sets.append(torch.from_numpy(idx).to(dev))
     pool = W.make_pool_torch(wl, dev)
+    if args.layout == "VK":
+        pool = pool.transpose(-1, -2).contiguous()
     act = torch.bfloat16 if wl.act == W.ACT_BF16 else torch.float32
     out = torch.empty(inp.num_tokens, wl.num_v_heads, wl.head_v_dim, dtype=act, device=dev)
     inter = None
     if wl.intermediates:
-        inter = torch.empty(inp.num_tokens, wl.num_v_heads, wl.head_k_dim, wl.head_v_dim,
+        inter = torch.empty((inp.num_tokens, wl.num_v_heads) + tuple(pool.shape[2:]),
                             dtype=torch.float32, device=dev)
     # the oracle's copy of the first set's initial states, taken before any update
     pool_rows0 = None
     if args.cpu_budget > 0:
         pool_rows0 = pool[idx_sets[0].clamp(min=0).long()].cpu().numpy()
+        if args.layout == "VK":
+            pool_rows0 = np.ascontiguousarray(np.swapaxes(pool_rows0, -1, -2))
 
     stream = torch.cuda.current_stream(dev)
 
@@ -256,7 +265,8 @@ def main():
         gdn.gdn_gating_delta_rule_update(
             d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool,
             idx_sets[i % sets], d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
-            block_v=args.block_v, waves_per_group=args.waves, stream=stream.cuda_stream)
+            kernel_family=args.family, block_v=args.block_v, block_k=args.block_k,
+            waves_per_group=args.waves, stream=stream.cuda_stream, state_layout=args.layout)
 
     for i in range(args.warmup):
         step(i)
@@ -279,8 +289,11 @@ def main():
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     value = updates * args.steps / wall
     info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
-                                        tokens_per_seq=wl.tokens_per_seq, block_v=args.block_v,
-                                        waves_per_group=args.waves), d["cu_seqlens"] is not None)
+                                        tokens_per_seq=wl.tokens_per_seq,
+                                        kernel_family=args.family, block_v=args.block_v,
+                                        block_k=args.block_k, waves_per_group=args.waves,
+                                        state_layout=args.layout),
+                        d["cu_seqlens"] is not None)
 
     res = {
         "metric": METRIC,
@@ -298,8 +311,10 @@ def main():
         "config": {"workload": wl.name, "num_seqs": B, "tokens": inp.num_tokens,
                    "num_k_heads": wl.num_k_heads, "num_v_heads": wl.num_v_heads,
                    "head_k_dim": wl.head_k_dim, "head_v_dim": wl.head_v_dim,
-                   "activations": wl.act, "state": "f32", "pool_slots": wl.num_slots,
-                   "slot_sets": sets, "block_v": info.block_v,
+                   "activations": wl.act, "state": "f32", "state_layout": args.layout,
+                   "pool_slots": wl.num_slots,
+                   "slot_sets": sets, "kernel": KERNEL_NAMES[info.kernel_family],
+                   "block_v": info.block_v, "block_k": info.block_k,
                    "waves_per_group": info.waves_per_group, "workgroups": info.workgroups,
                    "parallelism": "single GPU"},
         "hbm_gb_s": achieved,

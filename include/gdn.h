@@ -21,7 +21,8 @@
  *   out[t,h] = S^T qhat
  *
  * S is the K x V fp32 state of (sequence, v-head), gathered from and written
- * back to a slot-indexed pool.  One call covers T=1 decode, fixed-T
+ * back to a slot-indexed pool, stored either with V fastest (GDN_LAYOUT_KV,
+ * the default) or transposed with K fastest (GDN_LAYOUT_VK).  One call covers T=1 decode, fixed-T
  * multi-token verification and varlen sequences (cu_seqlens), with optional
  * per-token intermediate states.
  *
@@ -75,6 +76,13 @@ typedef enum gdn_dtype {
  * on `stream`; meant for tests and debugging. */
 #define GDN_FLAG_DEBUG_CHECKS 0x2u
 
+/* Storage order of each K x V state tile in the pool and in
+ * intermediate_states.  The layout is a property of the caller's buffers. */
+#define GDN_LAYOUT_KV 0 /* element (kappa, c) at kappa*V + c (V fastest)      */
+#define GDN_LAYOUT_VK 1 /* element (kappa, c) at c*K + kappa (K fastest): each
+                           value-row is contiguous; served by the value-row
+                           kernel, whose wavefronts never synchronise        */
+
 typedef struct gdn_config {
     int32_t num_seqs;        /* B >= 0 sequences (B = 0: nothing is launched)   */
     int32_t tokens_per_seq;  /* T >= 1 tokens per sequence when cu_seqlens is
@@ -95,25 +103,37 @@ typedef struct gdn_config {
     int64_t k_stride_tok;    /* same for k                                       */
     int64_t v_stride_tok;    /* same for v (dense = H_v*V)                       */
     uint32_t flags;          /* GDN_FLAG_*                                       */
-    int32_t block_v;         /* 0 = library choice (row-split kernel for one token
-                                per sequence, 32-column tiles otherwise); else
-                                force the column-tile kernel with 8, 16, 32 or
-                                64 columns per wavefront (dividing V)            */
-    int32_t waves_per_group; /* 0 = library choice; else force the column-tile
-                                kernel with 1..8 wavefronts per workgroup,
-                                dividing G*V/block_v                             */
+    int32_t state_layout;    /* GDN_LAYOUT_KV (0) or GDN_LAYOUT_VK (1)           */
+    /* Tiling overrides (0 = the library's static table).  They change the
+     * order of the fp32 reductions, never the operation. */
+    int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): with GDN_LAYOUT_KV, row split
+                                for one token per sequence and column tiles
+                                otherwise; with GDN_LAYOUT_VK, value rows       */
+    int32_t block_v;         /* column tiles: 8, 16, 32 or 64 V-columns per
+                                wavefront (dividing V).  A non-zero value with
+                                GDN_KERNEL_AUTO selects the column tiles        */
+    int32_t block_k;         /* row split: K-rows per wavefront (rows per lane
+                                16 or 8 times the rows one instruction covers) */
+    int32_t waves_per_group; /* wavefronts per workgroup, 1..8: column tiles:
+                                dividing G*V/block_v; row split: a multiple of
+                                K/block_k covering a divisor of G heads        */
 } gdn_config;
 
-/* Kernel families (gdn_launch_info.kernel_family). */
-#define GDN_KERNEL_COLUMN_TILES 0 /* wavefront = (v-head, block_v columns, all K
+/* Kernel families (gdn_config.kernel_family, gdn_launch_info.kernel_family). */
+#define GDN_KERNEL_AUTO 0
+#define GDN_KERNEL_COLUMN_TILES 1 /* wavefront = (v-head, block_v columns, all K
                                      rows); any number of tokens               */
-#define GDN_KERNEL_ROW_SPLIT 1    /* wavefront = (v-head, all V columns, a block
-                                     of K rows); single-token decode           */
+#define GDN_KERNEL_ROW_SPLIT 2    /* wavefront = (v-head, all V columns, block_k
+                                     rows); one token per sequence             */
+#define GDN_KERNEL_VALUE_ROWS 3   /* GDN_LAYOUT_VK only: wavefront = (v-head,
+                                     block of whole value-rows); any number of
+                                     tokens                                    */
 
 /* Describes the launch that a configuration maps to (gdn_plan). */
 typedef struct gdn_launch_info {
-    int32_t kernel_family;    /* GDN_KERNEL_*                                */
+    int32_t kernel_family;    /* GDN_KERNEL_COLUMN_TILES or _ROW_SPLIT       */
     int32_t block_v;          /* V-columns per wavefront                     */
+    int32_t block_k;          /* K-rows per wavefront                        */
     int32_t waves_per_group;  /* wavefronts per workgroup                    */
     int32_t tokens_per_chunk; /* tokens staged in LDS at a time              */
     int32_t multi_token;      /* 0: single-token decode kernel; 1: token loop */
@@ -133,14 +153,16 @@ void gdn_default_config(gdn_config* cfg);
  *  v        [N, H_v, V]   act_dtype; token stride v_stride_tok
  *  a, b     [N, H_v]      act_dtype, dense
  *  A_log, dt_bias [H_v]   fp32
- *  state_pool [num_slots, H_v, K, V] fp32, V fastest; updated in place
+ *  state_pool [num_slots, H_v, K, V] fp32 (GDN_LAYOUT_KV) or
+ *             [num_slots, H_v, V, K] (GDN_LAYOUT_VK); updated in place
  *  state_idx  [B] int32: pool slot of sequence i; any negative value marks a
  *             padded sequence, which is skipped entirely (its pool rows, out
  *             rows and intermediate rows are neither read nor written)
  *  cu_seqlens [B+1] int32 token offsets, or NULL for T tokens per sequence.
  *             A zero-length sequence is skipped like a padded one.
  *  out      [N, H_v, V]   act_dtype, dense; bf16 is rounded to nearest even
- *  intermediate_states [N, H_v, K, V] fp32 or NULL: row t receives S after
+ *  intermediate_states [N, H_v, K, V] fp32 (same tile layout as the pool) or
+ *             NULL: row t receives S after
  *             token t (so the last token's row equals the final state)
  *
  * Alignment: q, k, v, out, state_pool and intermediate_states 16-byte

@@ -22,8 +22,14 @@ GDN_DTYPE_F32 = 0
 GDN_DTYPE_BF16 = 1
 GDN_FLAG_NO_FINAL_WRITEBACK = 0x1
 GDN_FLAG_DEBUG_CHECKS = 0x2
-GDN_KERNEL_COLUMN_TILES = 0
-GDN_KERNEL_ROW_SPLIT = 1
+GDN_KERNEL_AUTO = 0
+GDN_KERNEL_COLUMN_TILES = 1
+GDN_KERNEL_ROW_SPLIT = 2
+GDN_KERNEL_VALUE_ROWS = 3
+GDN_LAYOUT_KV = 0
+GDN_LAYOUT_VK = 1
+_LAYOUTS = {"KV": GDN_LAYOUT_KV, "VK": GDN_LAYOUT_VK, GDN_LAYOUT_KV: GDN_LAYOUT_KV,
+            GDN_LAYOUT_VK: GDN_LAYOUT_VK}
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
                 3: "GDN_ERR_UNSUPPORTED_SHAPE", 4: "GDN_ERR_UNSUPPORTED_DTYPE",
@@ -42,13 +48,15 @@ class GdnConfig(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("l2norm_eps", ctypes.c_float), ("q_stride_tok", ctypes.c_int64),
                 ("k_stride_tok", ctypes.c_int64), ("v_stride_tok", ctypes.c_int64),
-                ("flags", ctypes.c_uint32), ("block_v", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("state_layout", ctypes.c_int32),
+                ("kernel_family", ctypes.c_int32),
+                ("block_v", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("waves_per_group", ctypes.c_int32)]
 
 
 class GdnLaunchInfo(ctypes.Structure):
     _fields_ = [("kernel_family", ctypes.c_int32), ("block_v", ctypes.c_int32),
-                ("waves_per_group", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("waves_per_group", ctypes.c_int32),
                 ("tokens_per_chunk", ctypes.c_int32), ("multi_token", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("threads_per_group", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32)]
@@ -122,7 +130,7 @@ def _ptr(t) -> Optional[int]:
 
 
 def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
-                   intermediate_states):
+                   intermediate_states, state_layout=GDN_LAYOUT_KV):
     """dtype/shape/device/layout checks the C-ABI cannot make on raw pointers."""
     import torch
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
@@ -141,9 +149,11 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
     for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
         if t.dtype != torch.float32 or tuple(t.shape) != (Hv,) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 [{Hv}] tensor")
+    tile = (K, V) if _LAYOUTS[state_layout] == GDN_LAYOUT_KV else (V, K)
     if (state_pool.dtype != torch.float32 or state_pool.dim() != 4
-            or tuple(state_pool.shape[1:]) != (Hv, K, V) or not state_pool.is_contiguous()):
-        raise ValueError(f"state_pool must be a contiguous float32 [slots, {Hv}, {K}, {V}] tensor")
+            or tuple(state_pool.shape[1:]) != (Hv,) + tile or not state_pool.is_contiguous()):
+        raise ValueError(f"state_pool must be a contiguous float32 [slots, {Hv}, {tile[0]}, "
+                         f"{tile[1]}] tensor")
     if state_idx.dtype != torch.int32 or state_idx.dim() != 1 or not state_idx.is_contiguous():
         raise ValueError("state_idx must be a contiguous int32 [B] tensor")
     B = state_idx.shape[0]
@@ -153,9 +163,10 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
         raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor")
     if intermediate_states is not None and (
             intermediate_states.dtype != torch.float32
-            or tuple(intermediate_states.shape) != (N, Hv, K, V)
+            or tuple(intermediate_states.shape) != (N, Hv) + tile
             or not intermediate_states.is_contiguous()):
-        raise ValueError("intermediate_states must be a contiguous float32 [N, H_v, K, V] tensor")
+        raise ValueError("intermediate_states must be a contiguous float32 tensor shaped like "
+                         "[N] + one pool row")
     dev = q.device
     for t in (k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
               intermediate_states):
@@ -166,8 +177,9 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
 
 
 def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=None,
-                scale: float = 0.0, eps: float = 1e-6, flags: int = 0, block_v: int = 0,
-                waves_per_group: int = 0, k=None) -> GdnConfig:
+                scale: float = 0.0, eps: float = 1e-6, flags: int = 0, kernel_family: int = 0,
+                block_v: int = 0, block_k: int = 0, waves_per_group: int = 0,
+                k=None, state_layout=GDN_LAYOUT_KV) -> GdnConfig:
     """Sizes and strides of a call, read off the tensors' shapes."""
     import torch
     N, Hk, K = q.shape
@@ -181,6 +193,7 @@ def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=
     cfg.num_tokens = N
     cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim = Hk, Hv, K, V
     cfg.num_slots = state_pool.shape[0]
+    cfg.state_layout = _LAYOUTS[state_layout]
     if q.dtype == torch.bfloat16:
         cfg.act_dtype = GDN_DTYPE_BF16
     elif q.dtype == torch.float32:
@@ -194,7 +207,9 @@ def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=
             raise ValueError("heads must be dense within a token (strides [*, D, 1])")
         setattr(cfg, name, t.stride(0) if t.shape[0] > 1 else 0)
     cfg.flags = flags
+    cfg.kernel_family = kernel_family
     cfg.block_v = block_v
+    cfg.block_k = block_k
     cfg.waves_per_group = waves_per_group
     return cfg
 
@@ -202,22 +217,25 @@ def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=
 def gdn_gating_delta_rule_update(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx,
                                  cu_seqlens=None, out=None, intermediate_states=None, *,
                                  tokens_per_seq=None, scale: float = 0.0, eps: float = 1e-6,
-                                 flags: int = 0, block_v: int = 0, waves_per_group: int = 0,
-                                 stream=None):
+                                 flags: int = 0, kernel_family: int = 0, block_v: int = 0,
+                                 block_k: int = 0, waves_per_group: int = 0, stream=None,
+                                 state_layout=GDN_LAYOUT_KV):
     """Enqueue the fused update on ``stream`` (default: torch's current stream
     on q's device).  Shapes: q, k [N, H_k, K]; v [N, H_v, V]; a, b [N, H_v];
     A_log, dt_bias [H_v] fp32; state_pool [slots, H_v, K, V] fp32 (updated in
     place); state_idx [B] int32; cu_seqlens [B+1] int32 or None; out [N, H_v, V]
     (allocated like v when None); intermediate_states [N, H_v, K, V] fp32 or
-    None.  Returns ``out``."""
+    None.  With state_layout "VK" (GDN_LAYOUT_VK) the pool is [slots, H_v, V, K]
+    and intermediate_states [N, H_v, V, K].  Returns ``out``."""
     import torch
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
-                   intermediate_states)
+                   intermediate_states, state_layout)
     cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
-                      scale=scale, eps=eps, flags=flags, block_v=block_v,
-                      waves_per_group=waves_per_group, k=k)
+                      scale=scale, eps=eps, flags=flags, kernel_family=kernel_family,
+                      block_v=block_v, block_k=block_k, waves_per_group=waves_per_group, k=k,
+                      state_layout=state_layout)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):

@@ -45,6 +45,135 @@ int default_waves(int units) {
     return 1;
 }
 
+// Chooses the kernel family, tile and grid of a (size-checked) config, and
+// rejects tiling overrides that have no kernel instance.  Single-token calls
+// default to the row-split kernel (one contiguous kilobyte per load/store
+// instruction); multi-token calls, and calls that override block_v, use the
+// column-tile kernel.
+gdn_status plan_launch(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    s.K = K;
+    s.act = c.act_dtype;
+    s.multi_token = (has_cu || c.tokens_per_seq > 1) ? 1 : 0;
+    s.chunk = s.multi_token ? gdn::kChunkTokens : 1;
+    if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_COLUMN_TILES &&
+        c.kernel_family != GDN_KERNEL_ROW_SPLIT && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
+        return fail(GDN_ERR_BAD_ARGUMENT, "kernel_family = %d is not a GDN_KERNEL_* value",
+                    c.kernel_family);
+    if (c.waves_per_group < 0 || c.waves_per_group > 8)
+        return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d is not in 0..8", c.waves_per_group);
+    if (c.state_layout != GDN_LAYOUT_KV && c.state_layout != GDN_LAYOUT_VK)
+        return fail(GDN_ERR_BAD_ARGUMENT, "state_layout = %d is neither GDN_LAYOUT_KV nor _VK",
+                    c.state_layout);
+
+    if (c.state_layout == GDN_LAYOUT_VK) {
+        if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
+            return fail(GDN_ERR_BAD_ARGUMENT, "GDN_LAYOUT_VK is served by GDN_KERNEL_VALUE_ROWS only");
+        if (c.block_v != 0 || c.block_k != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "block_v/block_k do not apply to GDN_LAYOUT_VK");
+        const int rpw = gdn::vk_rows_per_wave(K, V);
+        if (rpw == 0)
+            return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no value-row kernel for K = %d, V = %d", K, V);
+        // wavefront units per k-head: G v-heads x V/rpw row blocks; the
+        // wavefronts never synchronise, so any divisor may form a workgroup
+        const int units = G * (V / rpw);
+        if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/%d = %d",
+                        c.waves_per_group, rpw, units);
+        s.kind = gdn::kKindValueRows;
+        s.block_v = rpw;
+        s.block_k = K;
+        s.rows_rpl_max = 0;
+        s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
+        if (s.groups > INT32_MAX)
+            return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
+                        static_cast<long long>(s.groups));
+        s.lds_bytes = gdn::lds_bytes_for(s, V);
+        return GDN_OK;
+    }
+    if (c.kernel_family == GDN_KERNEL_VALUE_ROWS)
+        return fail(GDN_ERR_BAD_ARGUMENT, "GDN_KERNEL_VALUE_ROWS needs GDN_LAYOUT_VK");
+
+    bool rows;
+    if (c.kernel_family == GDN_KERNEL_ROW_SPLIT) {
+        if (s.multi_token)
+            return fail(GDN_ERR_BAD_ARGUMENT,
+                        "the row-split kernel handles one token per sequence (no cu_seqlens, T = 1)");
+        if (c.block_v != 0 && c.block_v != V)
+            return fail(GDN_ERR_BAD_ARGUMENT, "the row-split kernel covers all V columns "
+                                              "(block_v must be 0 or V = %d)", V);
+        rows = true;
+    } else if (c.kernel_family == GDN_KERNEL_COLUMN_TILES) {
+        rows = false;
+    } else {
+        rows = !s.multi_token && c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0;
+    }
+
+    if (rows) {
+        int rpl_max = 16;
+        if (c.block_k != 0) {
+            rpl_max = 0;
+            for (int r : {16, 8})
+                if (gdn::rows_per_wave(K, V, r) == c.block_k) { rpl_max = r; break; }
+            if (!rpl_max)
+                return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
+                                                  "wavefront for K = %d, V = %d", c.block_k, K, V);
+        }
+        const int rpw = gdn::rows_per_wave(K, V, rpl_max);
+        if (rpw == 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel for K = %d, V = %d", K, V);
+        const int kw = K / rpw;
+        int heads = 0;
+        if (c.waves_per_group != 0) {
+            if (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0)
+                return fail(GDN_ERR_BAD_ARGUMENT,
+                            "waves_per_group = %d must be a multiple of the %d wavefronts per head "
+                            "covering a divisor of G = %d heads", c.waves_per_group, kw, G);
+            heads = c.waves_per_group / kw;
+        } else {
+            for (int hp = G; hp >= 1 && !heads; --hp)  // largest divisor of G within 8 waves
+                if (G % hp == 0 && hp * kw <= 8) heads = hp;
+        }
+        s.kind = gdn::kKindRows;
+        s.block_v = V;
+        s.block_k = rpw;
+        s.rows_rpl_max = rpl_max;
+        s.waves = heads * kw;
+        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (G / heads);
+    } else {
+        if (c.block_k != 0 && c.block_k != K)
+            return fail(GDN_ERR_BAD_ARGUMENT, "the column-tile kernel covers all K rows "
+                                              "(block_k must be 0 or K = %d)", K);
+        if (c.block_v != 0) {
+            if (c.block_v != 8 && c.block_v != 16 && c.block_v != 32 && c.block_v != 64)
+                return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d is not 8, 16, 32 or 64", c.block_v);
+            if (V % c.block_v != 0)
+                return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d does not divide V = %d", c.block_v, V);
+            if (!gdn::instance_exists(K, c.block_v))
+                return fail(GDN_ERR_BAD_ARGUMENT, "no kernel for K = %d with block_v = %d", K,
+                            c.block_v);
+        }
+        const int bv = c.block_v ? c.block_v : default_block_v(c);
+        const int units = G * (V / bv);
+        if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/block_v = %d",
+                        c.waves_per_group, units);
+        s.kind = gdn::kKindColumns;
+        s.block_v = bv;
+        s.block_k = K;
+        s.rows_rpl_max = 0;
+        s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
+    }
+    if (s.groups > INT32_MAX)
+        return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
+                    static_cast<long long>(s.groups));
+    s.lds_bytes = gdn::lds_bytes_for(s, V);
+    return GDN_OK;
+}
+
 gdn_status check_config(const gdn_config* cfg, bool has_cu) {
     if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
     const gdn_config& c = *cfg;
@@ -90,58 +219,8 @@ gdn_status check_config(const gdn_config* cfg, bool has_cu) {
             return fail(GDN_ERR_MISALIGNED, "%s = %lld is not a multiple of 8 elements", st.name,
                         static_cast<long long>(st.s));
     }
-    const int G = c.num_v_heads / c.num_k_heads;
-    if (c.block_v != 0) {
-        if (c.block_v != 8 && c.block_v != 16 && c.block_v != 32 && c.block_v != 64)
-            return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d is not 8, 16, 32 or 64", c.block_v);
-        if (c.head_v_dim % c.block_v != 0)
-            return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d does not divide V = %d", c.block_v,
-                        c.head_v_dim);
-        if (!gdn::instance_exists(c.head_k_dim, c.block_v))
-            return fail(GDN_ERR_BAD_ARGUMENT, "no kernel for K = %d with block_v = %d", c.head_k_dim,
-                        c.block_v);
-    }
-    const int bv = c.block_v ? c.block_v : default_block_v(c);
-    const int units = G * (c.head_v_dim / bv);
-    if (c.waves_per_group != 0) {
-        if (c.waves_per_group < 1 || c.waves_per_group > 8 || units % c.waves_per_group != 0)
-            return fail(GDN_ERR_BAD_ARGUMENT,
-                        "waves_per_group = %d must be in 1..8 and divide G*V/block_v = %d",
-                        c.waves_per_group, units);
-    }
-    const int w = c.waves_per_group ? c.waves_per_group : default_waves(units);
-    const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / w);
-    if (groups > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
-                                        static_cast<long long>(groups));
-    return GDN_OK;
-}
-
-// Single-token calls without a tiling override use the row-split kernel
-// (contiguous kilobyte per load/store instruction); everything else uses the
-// column-tile kernel.
-void make_shape(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
-    const int G = c.num_v_heads / c.num_k_heads;
-    s.K = c.head_k_dim;
-    s.act = c.act_dtype;
-    s.multi_token = (has_cu || c.tokens_per_seq > 1) ? 1 : 0;
-    s.chunk = s.multi_token ? gdn::kChunkTokens : 1;
-    const int kw = gdn::rows_waves_per_head(c.head_k_dim, c.head_v_dim);
-    if (!s.multi_token && c.block_v == 0 && c.waves_per_group == 0 && kw > 0) {
-        s.kind = gdn::kKindRows;
-        s.block_v = c.head_v_dim;
-        int heads = 1;  // v-heads per workgroup: largest divisor of G within 8 waves
-        for (int hp = G; hp >= 1; --hp)
-            if (G % hp == 0 && hp * kw <= 8) { heads = hp; break; }
-        s.waves = heads * kw;
-        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (G / heads);
-    } else {
-        s.kind = gdn::kKindColumns;
-        s.block_v = c.block_v ? c.block_v : default_block_v(c);
-        const int units = G * (c.head_v_dim / s.block_v);
-        s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
-        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
-    }
-    s.lds_bytes = gdn::lds_bytes_for(s, c.head_v_dim);
+    gdn::LaunchShape sh{};
+    return plan_launch(c, has_cu, sh);
 }
 
 gdn_status debug_check_indices(const gdn_config& c, const int32_t* state_idx,
@@ -222,8 +301,12 @@ gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* 
     gdn_status s = check_config(cfg, has_cu_seqlens != 0);
     if (s != GDN_OK) return s;
     gdn::LaunchShape sh{};
-    make_shape(*cfg, has_cu_seqlens != 0, sh);
-    info->kernel_family = sh.kind;
+    s = plan_launch(*cfg, has_cu_seqlens != 0, sh);
+    if (s != GDN_OK) return s;
+    info->kernel_family = sh.kind == gdn::kKindRows        ? GDN_KERNEL_ROW_SPLIT
+                          : sh.kind == gdn::kKindValueRows ? GDN_KERNEL_VALUE_ROWS
+                                                           : GDN_KERNEL_COLUMN_TILES;
+    info->block_k = sh.block_k;
     info->block_v = sh.block_v;
     info->waves_per_group = sh.waves;
     info->tokens_per_chunk = sh.chunk;
@@ -252,7 +335,8 @@ gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void
     }
     const bool has_cu = cu_seqlens != nullptr;
     gdn::LaunchShape sh{};
-    make_shape(c, has_cu, sh);
+    s = plan_launch(c, has_cu, sh);
+    if (s != GDN_OK) return s;
 
     gdn::FusedParams p{};
     p.q = q;
@@ -287,10 +371,11 @@ gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void
     }();
     if (log)
         std::fprintf(stderr,
-                     "[gdn] %s K=%d V=%d act=%s multi_token=%d block_v=%d waves=%d chunk=%d "
-                     "groups=%lld lds=%d\n",
-                     sh.kind == gdn::kKindRows ? "rows" : "columns", sh.K, c.head_v_dim,
-                     sh.act ? "bf16" : "f32", sh.multi_token, sh.block_v,
+                     "[gdn] %s K=%d V=%d act=%s multi_token=%d block_v=%d block_k=%d waves=%d "
+                     "chunk=%d groups=%lld lds=%d\n",
+                     sh.kind == gdn::kKindRows ? "rows" : sh.kind == gdn::kKindValueRows ? "value-rows" : "columns",
+                     sh.K, c.head_v_dim,
+                     sh.act ? "bf16" : "f32", sh.multi_token, sh.block_v, sh.block_k,
                      sh.waves, sh.chunk, static_cast<long long>(sh.groups), sh.lds_bytes);
 
     const hipError_t e = gdn::launch_fused(sh, p, st);

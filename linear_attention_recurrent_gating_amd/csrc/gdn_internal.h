@@ -39,14 +39,17 @@ struct FusedParams {
 // Kernel families.
 constexpr int kKindColumns = 0;  // wave = (v-head, BV-column tile); any token count
 constexpr int kKindRows = 1;     // wave = (v-head, block of whole rows); one token
+constexpr int kKindValueRows = 2;  // transposed (VK) state: wave = (v-head, block of value-rows)
 
 struct LaunchShape {
     int kind;
     int K;
-    int block_v;
+    int block_v;      // columns per wavefront
+    int block_k;      // rows per wavefront
     int act;          // 0 = fp32, 1 = bf16
     int multi_token;  // 0: one token per sequence; 1: chunked token loop
     int waves;        // wavefronts per workgroup
+    int rows_rpl_max; // row-split kernel: at most 16 or 8 state rows per lane
     int chunk;        // tokens staged per chunk (1 for the single-token kernel)
     int64_t groups;   // grid size
     int lds_bytes;
@@ -61,9 +64,13 @@ int lds_bytes_for(const LaunchShape& shape, int V);
 // True when a column-tile kernel instance exists for (K, block_v).
 bool instance_exists(int K, int block_v);
 
-// Wavefronts per v-head of the row-split kernel for (K, V); 0 if it has no
-// instance for that pair.
-int rows_waves_per_head(int K, int V);
+// Rows per wavefront of the row-split kernel for (K, V) with at most rpl_max
+// (16 or 8) rows per lane; 0 if there is no such instance.
+int rows_per_wave(int K, int V, int rpl_max);
+
+// Value-rows per wavefront of the VK-layout kernel for (K, V); 0 if there is
+// no instance for that pair.
+int vk_rows_per_wave(int K, int V);
 
 // Enqueues the fused kernel; returns the HIP launch status.
 hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);

@@ -146,6 +146,13 @@ __device__ __forceinline__ void store4_act(void* base, int64_t e, float4 o) {
     }
 }
 
+// One output element (bf16 rounded to nearest even).
+template <int ACT>
+__device__ __forceinline__ void store1_act(void* base, int64_t e, float o) {
+    if constexpr (ACT == 0) static_cast<float*>(base)[e] = o;
+    else static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bf16_rne(o));
+}
+
 // ------------------------------------------------------------ cross-lane sums
 // Rotation by CTRL within 16-lane DPP rows (0x120 + n = row_ror:n).
 template <int CTRL>
@@ -185,6 +192,22 @@ __device__ __forceinline__ float sum_dpp_row(float x) {
     x += dpp_mov<0x124>(x);
     x += dpp_mov<0x122>(x);
     x += dpp_mov<0x121>(x);
+    return x;
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 2..64), leaving every
+// lane of a group with a bitwise identical sum: quad swaps, the half-row and
+// row mirrors, then the permlane16/32 swaps.  Each step pairs lanes that
+// already hold identical partial sums, and fp32 addition is commutative.
+template <int N>
+__device__ __forceinline__ float sum_lane_groups(float x) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "power-of-two group");
+    if constexpr (N >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
+    if constexpr (N >= 16) x += dpp_mov<0x140>(x);  // row_mirror
+    if constexpr (N >= 32) x = sum_xor16(x);
+    if constexpr (N >= 64) x = sum_xor32(x);
     return x;
 }
 
@@ -439,20 +462,60 @@ gdn_fused_update(const FusedParams p) {
 // reduced in-lane, across the wave's row groups with permlane swaps, and
 // across the KW wavefronts of the head through LDS, summed in a fixed order
 // so every wave derives the same u.
-template <int K, int V>
+template <int K, int V, int RPL_MAX>
 struct RowSplit {
-    static constexpr int LPR = V / 4;                          // lanes per row
-    static constexpr int RG = kWave / LPR;                     // rows per instruction
-    static constexpr int RPL = (K / RG < 16) ? K / RG : 16;    // rows per lane
-    static constexpr int RPW = RPL * RG;                       // rows per wave
-    static constexpr int KW = K / RPW;                         // waves per head
-    static constexpr int PART = 2 * V + 4;                     // partial sums per wave (floats)
+    static constexpr int LPR = V / 4;                                   // lanes per row
+    static constexpr int RG = kWave / LPR;                              // rows per instruction
+    static constexpr int RPL = (K / RG < RPL_MAX) ? K / RG : RPL_MAX;   // rows per lane
+    static constexpr int RPW = RPL * RG;                                // rows per wave
+    static constexpr int KW = K / RPW;                                  // waves per head
+    static constexpr int PART = 2 * V + 4;                              // partial sums per wave
 };
 
-template <int K, int V, int ACT>
+// The single token's q and k for the row-split kernel, in two halves so the
+// raw loads can be issued ahead of the state loads: DPP rows 0 and 1 of
+// wavefront 0 hold q and k, K/16 elements per lane.
+template <int K, int ACT>
+struct SingleTokenQK {
+    static constexpr int EPL = K / 16;
+    float x[EPL];
+    bool active, is_k;
+
+    __device__ __forceinline__ void load(const FusedParams& p, int j, int64_t t, int wave,
+                                         int lane) {
+        const int vec = wave * 4 + lane / 16;
+        active = vec < 2;
+        is_k = vec == 1;
+        if (active) {
+            const int lr = lane % 16;
+            if (is_k)
+                load_act<ACT, EPL>(p.k, t * p.k_stride + static_cast<int64_t>(j) * K + lr * EPL, x);
+            else
+                load_act<ACT, EPL>(p.q, t * p.q_stride + static_cast<int64_t>(j) * K + lr * EPL, x);
+        }
+    }
+
+    // Same arithmetic, in the same order, as stage_qk.
+    template <typename POS>
+    __device__ __forceinline__ void finish(const FusedParams& p, float* qs, float* ks, int lane,
+                                           POS pos) {
+        if (!active) return;
+        const int lr = lane % 16;
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+        ss = sum_dpp_row(ss);
+        const float f = (is_k ? 1.0f : p.scale) * rsqrtf(ss + p.eps);
+        float* dst = is_k ? ks : qs;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dst[pos(lr * EPL + e)] = x[e] * f;
+    }
+};
+
+template <int K, int V, int ACT, int RPL_MAX>
 __global__ void __launch_bounds__(kMaxThreads)
 gdn_decode_rows(const FusedParams p) {
-    using L = RowSplit<K, V>;
+    using L = RowSplit<K, V, RPL_MAX>;
     constexpr int LPR = L::LPR, RG = L::RG, RPL = L::RPL, RPW = L::RPW, KW = L::KW;
     static_assert(LPR >= 8 && RPL >= 1 && K % RPW == 0, "unsupported K/V pair");
 
@@ -482,6 +545,17 @@ gdn_decode_rows(const FusedParams p) {
     const int col = 4 * (lane % LPR);
     const int rg = lane / LPR;
 
+    // Small loads first (q/k for the staging rows, gates, v): they return
+    // while the state tile is still streaming in.
+    SingleTokenQK<K, ACT> qk;
+    qk.load(p, j, t, wave, lane);
+    const float a_t = load_scalar<ACT>(p.a, t * p.Hv + h);
+    const float b_t = load_scalar<ACT>(p.b, t * p.Hv + h);
+    const float A_log = p.A_log[h];
+    const float dt_bias = p.dt_bias[h];
+    float vv[4];
+    load_act<ACT, 4>(p.v, t * p.v_stride + static_cast<int64_t>(h) * V + col, vv);
+
     constexpr uint32_t tile_bytes = static_cast<uint32_t>(K * V * sizeof(float));
     const __amdgpu_buffer_rsrc_t tile_r =
         tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * (K * V), tile_bytes);
@@ -493,13 +567,10 @@ gdn_decode_rows(const FusedParams p) {
     for (int i = 0; i < RPL; ++i) S[i] = load_state(tile_r, lane_bytes, i * row_step);
 
     float gamma, beta;
-    gates(load_scalar<ACT>(p.a, t * p.Hv + h), load_scalar<ACT>(p.b, t * p.Hv + h), p.A_log[h],
-          p.dt_bias[h], gamma, beta);
-    float vv[4];
-    load_act<ACT, 4>(p.v, t * p.v_stride + static_cast<int64_t>(h) * V + col, vv);
+    gates(a_t, b_t, A_log, dt_bias, gamma, beta);
 
     // rows kw*RPW + RG*i + rg of the head sit at kw*RPW + rg*RPL + i
-    stage_qk<K, ACT>(p, qs, ks, j, t, 1, wave, waves, lane, [](int kappa) {
+    qk.finish(p, qs, ks, lane, [](int kappa) {
         const int r = kappa % RPW;
         return (kappa - r) + (r % RG) * RPL + r / RG;
     });
@@ -576,6 +647,308 @@ gdn_decode_rows(const FusedParams p) {
     }
 }
 
+
+// -------------------------------------------------------- value-row kernels
+// State stored transposed ("VK": each of the V value-rows holds its K key
+// entries contiguously).  A wavefront owns whole value-rows.  LPR = K/8 lanes
+// span one row and each lane holds keys 4c..4c+3 and 4(c+LPR)..+3
+// (c = lane % LPR), so a 128-bit instruction moves RG = 64/LPR rows, two
+// half-rows of 256 bytes per row at K = 128.  Lane l holds rows
+// vw*RPW + RG*i + l/LPR (i < RPL).  Every reduction over K -- the q/k norms,
+// S^T k, S^T q and k.q -- stays inside the wavefront (LPR-lane DPP/permlane
+// sums), and the update of value-row i needs only that row's u_i, so rows are
+// processed one after another.  The single-token kernel uses no LDS and no
+// barrier: its wavefronts never wait for each other.
+template <int K, int V>
+struct ValueRows {
+    static constexpr int CPL = 2;                                   // 128-bit chunks per lane per row
+    static constexpr int LPR = K / (4 * CPL);                       // lanes per row
+    static constexpr int RG = kWave / LPR;                          // rows per instruction
+    static constexpr int RPL = (V / RG < 8) ? V / RG : 8;           // rows per lane
+    static constexpr int RPW = RPL * RG;                            // rows per wave
+    static constexpr int VW = V / RPW;                              // waves per head
+    static constexpr uint32_t ROW_STEP = RG * K * sizeof(float);    // bytes between a lane's rows
+    static constexpr uint32_t HALF = LPR * 4 * sizeof(float);       // bytes between a lane's chunks
+};
+
+// Loads this lane's keys of one q or k vector: chunks at 4c and 4(c+LPR).
+template <int K, int ACT, int LPR>
+__device__ __forceinline__ void load_keys(const void* base, int64_t row, int c, float (&x)[8]) {
+    float lo[4], hi[4];
+    load_act<ACT, 4>(base, row + 4 * c, lo);
+    load_act<ACT, 4>(base, row + 4 * (c + LPR), hi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = lo[e]; x[4 + e] = hi[e]; }
+}
+
+// Normalises this lane's keys of q and k (sum of squares over the LPR lanes of
+// a row, one rsqrt each; q carries the query scale) and forms k.q.  Both
+// value-row kernels call it, so their norms round identically.
+template <int LPR>
+__device__ __forceinline__ void normalize_keys(const float (&qx)[8], const float (&kx)[8], float scale,
+                                               float eps, float (&qh)[8], float (&kh)[8], float& kq) {
+    float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        ssq = __builtin_fmaf(qx[e], qx[e], ssq);
+        ssk = __builtin_fmaf(kx[e], kx[e], ssk);
+    }
+    ssq = sum_lane_groups<LPR>(ssq);
+    ssk = sum_lane_groups<LPR>(ssk);
+    const float fq = scale * rsqrtf(ssq + eps);
+    const float fk = rsqrtf(ssk + eps);
+    kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        qh[e] = qx[e] * fq;
+        kh[e] = kx[e] * fk;
+        kq = __builtin_fmaf(kh[e], qh[e], kq);
+    }
+    kq = sum_lane_groups<LPR>(kq);
+}
+
+// One value-row step: S^T k and S^T q of row i (this lane's keys, then the
+// LPR-lane sum), u = beta*(v - gamma*S^T k), o = gamma*S^T q + u*(k.q), and
+// the decayed rank-1 update of the row.  Returns o.
+template <int LPR>
+__device__ __forceinline__ float value_row_step(float4 (&Si)[2], const float (&kh)[8],
+                                                const float (&qh)[8], float v, float gamma,
+                                                float beta, float kq) {
+    const float s8[8] = {Si[0].x, Si[0].y, Si[0].z, Si[0].w, Si[1].x, Si[1].y, Si[1].z, Si[1].w};
+    float pk = s8[0] * kh[0], pq = s8[0] * qh[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+        pk = __builtin_fmaf(s8[e], kh[e], pk);
+        pq = __builtin_fmaf(s8[e], qh[e], pq);
+    }
+    pk = sum_lane_groups<LPR>(pk);
+    pq = sum_lane_groups<LPR>(pq);
+    const float u = beta * (v - gamma * pk);
+    const float o = __builtin_fmaf(u, kq, gamma * pq);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        Si[hh].x = __builtin_fmaf(kh[4 * hh + 0], u, gamma * Si[hh].x);
+        Si[hh].y = __builtin_fmaf(kh[4 * hh + 1], u, gamma * Si[hh].y);
+        Si[hh].z = __builtin_fmaf(kh[4 * hh + 2], u, gamma * Si[hh].z);
+        Si[hh].w = __builtin_fmaf(kh[4 * hh + 3], u, gamma * Si[hh].w);
+    }
+    return o;
+}
+
+// Workgroup -> (sequence, k-head, slice of wavefront units); a unit is
+// (v-head of the GQA group, block of RPW value-rows).
+struct VkPlace {
+    int seq, j, h, vw;
+};
+
+template <int VW>
+__device__ __forceinline__ VkPlace vk_place(const FusedParams& p, int wave, int waves) {
+    int64_t blk = blockIdx.x;
+    const int gslice = static_cast<int>(blk % p.groups_per_khead);
+    blk /= p.groups_per_khead;
+    VkPlace pl;
+    pl.j = static_cast<int>(blk % p.Hk);
+    pl.seq = static_cast<int>(blk / p.Hk);
+    const int unit = gslice * waves + wave;
+    pl.h = pl.j * p.G + unit / VW;
+    pl.vw = unit % VW;
+    return pl;
+}
+
+template <int K, int V, int ACT>
+__global__ void __launch_bounds__(kMaxThreads)
+gdn_vk_decode(const FusedParams p) {
+    using L = ValueRows<K, V>;
+    constexpr int LPR = L::LPR, RG = L::RG, RPL = L::RPL, RPW = L::RPW, VW = L::VW;
+    static_assert(LPR >= 4 && RPL >= 1 && V % RPW == 0, "unsupported K/V pair");
+
+    const int waves = blockDim.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const VkPlace pl = vk_place<VW>(p, wave, waves);
+    const int32_t slot = p.state_idx[pl.seq];
+    if (slot < 0) return;  // padded: touch nothing
+    const int64_t t = pl.seq;
+    const int h = pl.h;
+    const int c = lane % LPR;
+    const int row0 = pl.vw * RPW + lane / LPR;   // this lane's rows: row0 + RG*i
+
+    // small loads first; they return while the state streams in
+    float qx[8], kx[8];
+    load_keys<K, ACT, LPR>(p.q, t * p.q_stride + static_cast<int64_t>(pl.j) * K, c, qx);
+    load_keys<K, ACT, LPR>(p.k, t * p.k_stride + static_cast<int64_t>(pl.j) * K, c, kx);
+    const float a_t = load_scalar<ACT>(p.a, t * p.Hv + h);
+    const float b_t = load_scalar<ACT>(p.b, t * p.Hv + h);
+    const float A_log = p.A_log[h];
+    const float dt_bias = p.dt_bias[h];
+    float vv[RPL];
+    const int64_t vbase = t * p.v_stride + static_cast<int64_t>(h) * V + row0;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) vv[i] = load_scalar<ACT>(p.v, vbase + RG * i);
+
+    constexpr uint32_t tile_bytes = static_cast<uint32_t>(K * V * sizeof(float));
+    const __amdgpu_buffer_rsrc_t tile_r =
+        tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * (K * V), tile_bytes);
+    const uint32_t lane_bytes = static_cast<uint32_t>((row0 * K + 4 * c) * sizeof(float));
+    float4 S[RPL][2];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            S[i][hh] = load_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF);
+
+    float qh[8], kh[8], kq;
+    normalize_keys<LPR>(qx, kx, p.scale, p.eps, qh, kh, kq);
+    float gamma, beta;
+    gates(a_t, b_t, A_log, dt_bias, gamma, beta);
+
+    const int64_t obase = (t * p.Hv + h) * static_cast<int64_t>(V) + row0;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const float o = value_row_step<LPR>(S[i], kh, qh, vv[i], gamma, beta, kq);
+        if (c == 0) store1_act<ACT>(p.out, obase + RG * i, o);
+    }
+    if (p.inter) {
+        const __amdgpu_buffer_rsrc_t it_r =
+            tile_rsrc(p.inter + (static_cast<size_t>(t) * p.Hv + h) * (K * V), tile_bytes);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                store_state(it_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+    }
+    if (p.write_final) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                store_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+    }
+}
+
+// Raw (widened) q and k of tokens [c0, c0+nt) into qs/ks ([nt][K] each),
+// spread over all lanes of the workgroup.
+template <int K, int ACT>
+__device__ __forceinline__ void stage_raw_qk(const FusedParams& p, float* qs, float* ks, int j,
+                                             int64_t c0, int nt, int tid, int threads) {
+    for (int e = tid * 4; e < 2 * nt * K; e += threads * 4) {
+        const int vec = e / K, kk = e % K;
+        const int tok = vec >> 1;
+        const bool is_k = vec & 1;
+        float x[4];
+        load_act<ACT, 4>(is_k ? p.k : p.q,
+                         (c0 + tok) * (is_k ? p.k_stride : p.q_stride) + static_cast<int64_t>(j) * K + kk, x);
+        *reinterpret_cast<float4*>((is_k ? ks : qs) + tok * K + kk) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+}
+
+// Multi-token value-row kernel: the token loop keeps the state in VGPRs;
+// chunks of CHUNK tokens of raw q/k (shared by the workgroup, one barrier per
+// chunk), of v (per wave) and of the gates (one token per lane) are staged in
+// LDS, and each wavefront normalises q/k itself exactly as the single-token
+// kernel does.
+template <int K, int V, int ACT, int CHUNK>
+__global__ void __launch_bounds__(kMaxThreads)
+gdn_vk_multi(const FusedParams p) {
+    using L = ValueRows<K, V>;
+    constexpr int LPR = L::LPR, RG = L::RG, RPL = L::RPL, RPW = L::RPW, VW = L::VW;
+    static_assert(LPR >= 4 && RPL >= 1 && V % RPW == 0, "unsupported K/V pair");
+
+    extern __shared__ __align__(16) float lds[];
+    float* qs = lds;                 // [CHUNK][K] raw q
+    float* ks = lds + CHUNK * K;     // [CHUNK][K] raw k
+
+    const int waves = blockDim.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const VkPlace pl = vk_place<VW>(p, wave, waves);
+    const int32_t slot = p.state_idx[pl.seq];
+    int64_t t0, t1;
+    if (p.cu_seqlens) {
+        t0 = p.cu_seqlens[pl.seq];
+        t1 = p.cu_seqlens[pl.seq + 1];
+    } else {
+        t0 = static_cast<int64_t>(pl.seq) * p.T;
+        t1 = t0 + p.T;
+    }
+    if (slot < 0 || t1 <= t0) return;  // padded or empty: touch nothing
+    const int h = pl.h;
+    const int c = lane % LPR;
+    const int rg = lane / LPR;
+    const int row0 = pl.vw * RPW + rg;
+    float* vs = lds + 2 * CHUNK * K + wave * (CHUNK * RPW);   // [CHUNK][RPW] this wave's v
+
+    constexpr uint32_t tile_bytes = static_cast<uint32_t>(K * V * sizeof(float));
+    const __amdgpu_buffer_rsrc_t tile_r =
+        tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * (K * V), tile_bytes);
+    const uint32_t lane_bytes = static_cast<uint32_t>((row0 * K + 4 * c) * sizeof(float));
+    float4 S[RPL][2];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            S[i][hh] = load_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF);
+
+    const float A_log = p.A_log[h];
+    const float dt_bias = p.dt_bias[h];
+
+    for (int64_t c0 = t0; c0 < t1; c0 += CHUNK) {
+        const int nt = static_cast<int>(t1 - c0 < CHUNK ? t1 - c0 : CHUNK);
+        stage_raw_qk<K, ACT>(p, qs, ks, pl.j, c0, nt, threadIdx.x, blockDim.x);
+        float gam = 1.0f, bet = 0.0f;   // lane tau holds token tau's gates
+        if (lane < nt)
+            gates(load_scalar<ACT>(p.a, (c0 + lane) * p.Hv + h),
+                  load_scalar<ACT>(p.b, (c0 + lane) * p.Hv + h), A_log, dt_bias, gam, bet);
+        // v of this wave's rows, permuted so lane (rg, i) reads rg*RPL + i
+        for (int e = lane; e < nt * RPW; e += kWave) {
+            const int tok = e / RPW, r = e % RPW;
+            vs[tok * RPW + (r % RG) * RPL + r / RG] =
+                load_scalar<ACT>(p.v, (c0 + tok) * p.v_stride + static_cast<int64_t>(h) * V +
+                                          pl.vw * RPW + r);
+        }
+        lds_barrier();
+
+        for (int tau = 0; tau < nt; ++tau) {
+            const int64_t t = c0 + tau;
+            const float gamma = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), tau));
+            const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bet), tau));
+            float kx[8], qx[8], vv[RPL];
+            lds_read<4>(ks + tau * K + 4 * c, reinterpret_cast<float(&)[4]>(kx[0]));
+            lds_read<4>(ks + tau * K + 4 * (c + LPR), reinterpret_cast<float(&)[4]>(kx[4]));
+            lds_read<4>(qs + tau * K + 4 * c, reinterpret_cast<float(&)[4]>(qx[0]));
+            lds_read<4>(qs + tau * K + 4 * (c + LPR), reinterpret_cast<float(&)[4]>(qx[4]));
+            lds_read<RPL>(vs + tau * RPW + rg * RPL, vv);
+            float kh[8], qh[8], kq;
+            normalize_keys<LPR>(qx, kx, p.scale, p.eps, qh, kh, kq);
+
+            const int64_t obase = (t * p.Hv + h) * static_cast<int64_t>(V) + row0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const float o = value_row_step<LPR>(S[i], kh, qh, vv[i], gamma, beta, kq);
+                if (c == 0) store1_act<ACT>(p.out, obase + RG * i, o);
+            }
+            if (p.inter) {
+                const __amdgpu_buffer_rsrc_t it_r =
+                    tile_rsrc(p.inter + (static_cast<size_t>(t) * p.Hv + h) * (K * V), tile_bytes);
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        store_state(it_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+            }
+        }
+        if (c0 + CHUNK < t1) lds_barrier();   // the next chunk reuses the LDS
+    }
+
+    if (p.write_final) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                store_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+    }
+}
+
 // ------------------------------------------------------------ instance table
 using KernelFn = void (*)(FusedParams);
 
@@ -616,67 +989,107 @@ KernelFn select_columns(int K, int BV, int act, int multi_token) {
     return multi_token ? by_k<1, kChunkTokens>(K, BV) : by_k<1, 1>(K, BV);
 }
 
-template <int K, int V, int ACT>
+// Row-split instances: RPL_MAX 16 (64 state VGPRs per lane) and 8 (32),
+// while a head needs at most 8 wavefronts.
+template <int K, int V, int ACT, int RPLM>
 KernelFn pick_rows() {
-    if constexpr (RowSplit<K, V>::KW <= 8) return &gdn_decode_rows<K, V, ACT>;
+    if constexpr (RowSplit<K, V, RPLM>::KW <= 8) return &gdn_decode_rows<K, V, ACT, RPLM>;
     else return nullptr;
 }
 
+template <int K, int V, int ACT>
+KernelFn rows_by_rpl(int rpl) {
+    return rpl == 8 ? pick_rows<K, V, ACT, 8>() : rpl == 16 ? pick_rows<K, V, ACT, 16>() : nullptr;
+}
+
 template <int K, int ACT>
-KernelFn rows_by_v(int V) {
+KernelFn rows_by_v(int V, int rpl) {
     switch (V) {
-        case 32: return pick_rows<K, 32, ACT>();
-        case 64: return pick_rows<K, 64, ACT>();
-        case 128: return pick_rows<K, 128, ACT>();
-        case 256: return pick_rows<K, 256, ACT>();
+        case 32: return rows_by_rpl<K, 32, ACT>(rpl);
+        case 64: return rows_by_rpl<K, 64, ACT>(rpl);
+        case 128: return rows_by_rpl<K, 128, ACT>(rpl);
+        case 256: return rows_by_rpl<K, 256, ACT>(rpl);
         default: return nullptr;
     }
 }
 
 template <int ACT>
-KernelFn rows_by_k(int K, int V) {
+KernelFn rows_by_k(int K, int V, int rpl) {
     switch (K) {
-        case 32: return rows_by_v<32, ACT>(V);
-        case 64: return rows_by_v<64, ACT>(V);
-        case 128: return rows_by_v<128, ACT>(V);
-        case 256: return rows_by_v<256, ACT>(V);
+        case 32: return rows_by_v<32, ACT>(V, rpl);
+        case 64: return rows_by_v<64, ACT>(V, rpl);
+        case 128: return rows_by_v<128, ACT>(V, rpl);
+        case 256: return rows_by_v<256, ACT>(V, rpl);
         default: return nullptr;
     }
 }
 
-KernelFn select_rows(int K, int V, int act) {
-    return act == 0 ? rows_by_k<0>(K, V) : rows_by_k<1>(K, V);
+KernelFn select_rows(int K, int V, int act, int rpl) {
+    return act == 0 ? rows_by_k<0>(K, V, rpl) : rows_by_k<1>(K, V, rpl);
+}
+
+template <int K, int V, int ACT>
+KernelFn pick_vk(int multi) {
+    return multi ? &gdn_vk_multi<K, V, ACT, kChunkTokens> : &gdn_vk_decode<K, V, ACT>;
+}
+
+template <int K, int ACT>
+KernelFn vk_by_v(int V, int multi) {
+    switch (V) {
+        case 32: return pick_vk<K, 32, ACT>(multi);
+        case 64: return pick_vk<K, 64, ACT>(multi);
+        case 128: return pick_vk<K, 128, ACT>(multi);
+        case 256: return pick_vk<K, 256, ACT>(multi);
+        default: return nullptr;
+    }
+}
+
+KernelFn select_vk(int K, int V, int act, int multi) {
+    switch (K) {
+        case 32: return act ? vk_by_v<32, 1>(V, multi) : vk_by_v<32, 0>(V, multi);
+        case 64: return act ? vk_by_v<64, 1>(V, multi) : vk_by_v<64, 0>(V, multi);
+        case 128: return act ? vk_by_v<128, 1>(V, multi) : vk_by_v<128, 0>(V, multi);
+        case 256: return act ? vk_by_v<256, 1>(V, multi) : vk_by_v<256, 0>(V, multi);
+        default: return nullptr;
+    }
 }
 
 template <int K, int V>
-int rows_kw_of() { return RowSplit<K, V>::KW; }
+int vk_rows_of() { return ValueRows<K, V>::RPW; }
 
 template <int K>
-int rows_kw_by_v(int V) {
+int vk_rows_by_v(int V) {
     switch (V) {
-        case 32: return rows_kw_of<K, 32>();
-        case 64: return rows_kw_of<K, 64>();
-        case 128: return rows_kw_of<K, 128>();
-        case 256: return rows_kw_of<K, 256>();
+        case 32: return vk_rows_of<K, 32>();
+        case 64: return vk_rows_of<K, 64>();
+        case 128: return vk_rows_of<K, 128>();
+        case 256: return vk_rows_of<K, 256>();
         default: return 0;
     }
 }
 
 }  // namespace
 
+int vk_rows_per_wave(int K, int V) {
+    if (!select_vk(K, V, 0, 0)) return 0;
+    switch (K) {
+        case 32: return vk_rows_by_v<32>(V);
+        case 64: return vk_rows_by_v<64>(V);
+        case 128: return vk_rows_by_v<128>(V);
+        case 256: return vk_rows_by_v<256>(V);
+        default: return 0;
+    }
+}
+
 bool instance_exists(int K, int block_v) {
     return select_columns(K, block_v, 0, 0) != nullptr;
 }
 
-int rows_waves_per_head(int K, int V) {
-    if (!select_rows(K, V, 0)) return 0;
-    switch (K) {
-        case 32: return rows_kw_by_v<32>(V);
-        case 64: return rows_kw_by_v<64>(V);
-        case 128: return rows_kw_by_v<128>(V);
-        case 256: return rows_kw_by_v<256>(V);
-        default: return 0;
-    }
+int rows_per_wave(int K, int V, int rpl_max) {
+    if (!select_rows(K, V, 0, rpl_max)) return 0;
+    const int rg = kWave / (V / 4);
+    const int rpl = K / rg < rpl_max ? K / rg : rpl_max;
+    return rpl * rg;
 }
 
 int lds_bytes_for(const LaunchShape& s, int V) {
@@ -684,12 +1097,15 @@ int lds_bytes_for(const LaunchShape& s, int V) {
     if (s.kind == kKindColumns && s.multi_token)
         floats += s.waves * s.chunk * s.block_v;             // per-wave v rows
     if (s.kind == kKindRows) floats += s.waves * (2 * V + 4);  // per-wave partial sums
+    if (s.kind == kKindValueRows)                             // single token: no LDS at all
+        floats = s.multi_token ? 2 * s.chunk * s.K + s.waves * s.chunk * s.block_v : 0;
     return floats * static_cast<int>(sizeof(float));
 }
 
 hipError_t launch_fused(const LaunchShape& s, const FusedParams& p, hipStream_t stream) {
-    KernelFn fn = s.kind == kKindRows ? select_rows(s.K, p.V, s.act)
-                                      : select_columns(s.K, s.block_v, s.act, s.multi_token);
+    KernelFn fn = s.kind == kKindRows        ? select_rows(s.K, p.V, s.act, s.rows_rpl_max)
+                  : s.kind == kKindValueRows ? select_vk(s.K, p.V, s.act, s.multi_token)
+                                             : select_columns(s.K, s.block_v, s.act, s.multi_token);
     if (!fn) return hipErrorInvalidDeviceFunction;
     void* args[] = {const_cast<FusedParams*>(&p)};
     return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<unsigned>(s.groups)),

@@ -46,7 +46,7 @@ def _load(path: str = _LIB):
                       ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                       ctypes.c_int64, ctypes.c_double, ctypes.c_double,
-                      ctypes.c_int, ctypes.c_int]
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int]
         f.restype = ctypes.c_int
         _libs[path] = lib
     return lib
@@ -59,9 +59,9 @@ def _ptr(arr: Optional[np.ndarray]):
 def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
            tokens_per_seq: int = 1, scale: float = 0.0, eps: float = 1e-6,
            intermediates: bool = False, no_final_writeback: bool = False,
-           threads: int = 0, lib_path: str = _LIB):
-    """Run the oracle.  ``pool`` (float32 [slots, H_v, K, V]) is updated in
-    place.  Returns ``(out, inter)``: out is float64 [N, H_v, V] (rows of
+           threads: int = 0, lib_path: str = _LIB, state_layout: str = "KV"):
+    """Run the oracle.  ``pool`` (float32 [slots, H_v, K, V], or [slots, H_v,
+    V, K] with state_layout "VK") is updated in place.  Returns ``(out, inter)``: out is float64 [N, H_v, V] (rows of
     untouched tokens stay NaN), inter is float32 [N, H_v, K, V] (NaN where not
     written) or None.  ``lib_path`` selects another build of the same source."""
     lib = _load(lib_path)
@@ -81,17 +81,20 @@ def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
     Hv, V = v.shape[1], v.shape[2]
     if k.shape != q.shape or v.shape[0] != N or a.shape != (N, Hv) or b.shape != (N, Hv):
         raise ValueError("inconsistent activation shapes")
-    if pool.shape[1:] != (Hv, K, V):
-        raise ValueError("pool shape must be [slots, H_v, K, V]")
+    if state_layout not in ("KV", "VK"):
+        raise ValueError("state_layout must be 'KV' or 'VK'")
+    tile = (K, V) if state_layout == "KV" else (V, K)
+    if pool.shape[1:] != (Hv,) + tile:
+        raise ValueError(f"pool shape must be [slots, H_v, {tile[0]}, {tile[1]}]")
     out = np.full((N, Hv, V), np.nan, dtype=d)
-    inter = np.full((N, Hv, K, V), np.nan, dtype=np.float32) if intermediates else None
+    inter = np.full((N, Hv) + tile, np.nan, dtype=np.float32) if intermediates else None
     B = idx.shape[0]
     rc = lib.gdn_oracle_update(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                _ptr(A_log), _ptr(dt_bias), _ptr(pool), _ptr(idx),
                                _ptr(cu), _ptr(out), _ptr(inter),
                                B, tokens_per_seq, N, Hk, Hv, K, V, pool.shape[0],
                                float(scale), float(eps), int(no_final_writeback),
-                               int(threads))
+                               0 if state_layout == "KV" else 1, int(threads))
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out, inter
@@ -99,7 +102,7 @@ def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
 
 def run_inputs(inp, pool: np.ndarray, scale: float = 0.0, eps: float = 1e-6,
                intermediates: Optional[bool] = None, no_final_writeback=False,
-               threads: int = 0):
+               threads: int = 0, state_layout: str = "KV"):
     """Run the oracle on a ``workloads.HostInputs`` bundle."""
     wl = inp.wl
     if intermediates is None:
@@ -108,4 +111,5 @@ def run_inputs(inp, pool: np.ndarray, scale: float = 0.0, eps: float = 1e-6,
                   pool, inp.state_idx, inp.cu_seqlens,
                   tokens_per_seq=wl.tokens_per_seq, scale=scale, eps=eps,
                   intermediates=intermediates,
-                  no_final_writeback=no_final_writeback, threads=threads)
+                  no_final_writeback=no_final_writeback, threads=threads,
+                  state_layout=state_layout)

@@ -23,7 +23,10 @@
  *
  * S is K x V (row index kappa over K, column over V), gathered from
  * pool[state_idx[i], h] and written back there after the sequence's last
- * token.  Readings where the pages are silent: eps sits inside the square
+ * token.  The pool stores each K x V tile either with V fastest ("KV",
+ * element (kappa, c) at kappa*V + c) or transposed with K fastest ("VK",
+ * element (kappa, c) at c*K + kappa); intermediate states use the same
+ * layout.  Readings where the pages are silent: eps sits inside the square
  * root; a sequence with state_idx < 0 or with no tokens is not touched at all;
  * intermediate_states[t, h] holds S after token t at global token row t.
  *
@@ -40,6 +43,9 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+#define ORACLE_LAYOUT_KV 0
+#define ORACLE_LAYOUT_VK 1
 
 #define ORACLE_OK 0
 #define ORACLE_ERR_ARG 1
@@ -81,6 +87,8 @@ static void oracle_l2norm(const double *x, double *y, int n, double eps, double 
  * cu_seqlens [B+1] or NULL (then sequence i owns rows [i*T, (i+1)*T))
  * intermediate [N, Hv, K, V] fp32 or NULL
  * no_final_writeback != 0 leaves the pool unchanged
+ * state_layout: ORACLE_LAYOUT_KV or ORACLE_LAYOUT_VK (storage order of the
+ *   pool and intermediate tiles)
  * scale <= 0 selects K^-1/2.  threads <= 0 uses the OpenMP default.
  */
 int gdn_oracle_update(const double *q, const double *k, const double *v,
@@ -91,10 +99,15 @@ int gdn_oracle_update(const double *q, const double *k, const double *v,
                       float *intermediate,
                       int B, int T, int64_t N, int Hk, int Hv, int K, int V,
                       int64_t num_slots, double scale, double eps,
-                      int no_final_writeback, int threads)
+                      int no_final_writeback, int state_layout, int threads)
 {
     if (B < 0 || K <= 0 || V <= 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0)
         return ORACLE_ERR_ARG;
+    if (state_layout != ORACLE_LAYOUT_KV && state_layout != ORACLE_LAYOUT_VK)
+        return ORACLE_ERR_ARG;
+    /* storage strides of S[kappa][c] inside a tile */
+    const size_t row_stride = state_layout == ORACLE_LAYOUT_KV ? (size_t)V : 1;
+    const size_t col_stride = state_layout == ORACLE_LAYOUT_KV ? 1 : (size_t)K;
     if (B == 0)
         return ORACLE_OK;
     if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !pool ||
@@ -151,8 +164,9 @@ int gdn_oracle_update(const double *q, const double *k, const double *v,
             continue;
         }
         float *tile = pool + ((size_t)slot * Hv + h) * (size_t)K * V;
-        for (size_t e = 0; e < (size_t)K * V; ++e)
-            S[e] = (double)tile[e];
+        for (int kk = 0; kk < K; ++kk)
+            for (int c = 0; c < V; ++c)
+                S[(size_t)kk * V + c] = (double)tile[kk * row_stride + c * col_stride];
 
         for (int64_t t = t0; t < t1; ++t) {
             /* gating: decay g and write strength beta */
@@ -188,13 +202,15 @@ int gdn_oracle_update(const double *q, const double *k, const double *v,
             }
             if (intermediate) {
                 float *it = intermediate + ((size_t)t * Hv + h) * (size_t)K * V;
-                for (size_t e = 0; e < (size_t)K * V; ++e)
-                    it[e] = (float)S[e];
+                for (int kk = 0; kk < K; ++kk)
+                    for (int c = 0; c < V; ++c)
+                        it[kk * row_stride + c * col_stride] = (float)S[(size_t)kk * V + c];
             }
         }
         if (!no_final_writeback)
-            for (size_t e = 0; e < (size_t)K * V; ++e)
-                tile[e] = (float)S[e];
+            for (int kk = 0; kk < K; ++kk)
+                for (int c = 0; c < V; ++c)
+                    tile[kk * row_stride + c * col_stride] = (float)S[(size_t)kk * V + c];
         free(S); free(kh); free(qh); free(u);
     }
     return status;

@@ -58,8 +58,15 @@ def live_rows(inp):
     return cat(live), cat(dead)
 
 
+def to_layout(pool_kv: np.ndarray, layout: str) -> np.ndarray:
+    """A [slots, H_v, K, V] pool (or one tile stack) in the given storage order."""
+    if layout == "KV":
+        return pool_kv
+    return np.ascontiguousarray(np.swapaxes(pool_kv, -1, -2))
+
+
 def run_gpu(inp, pool, device, intermediates=None, flags=0, block_v=0, waves_per_group=0,
-            tensors=None, stream=None):
+            tensors=None, stream=None, kernel_family=0, block_k=0, layout="KV"):
     """One call of the HIP path.  Returns (out, inter) as torch tensors; rows
     that must not be written are pre-filled with NaN."""
     import torch
@@ -73,12 +80,14 @@ def run_gpu(inp, pool, device, intermediates=None, flags=0, block_v=0, waves_per
     out = torch.full((N, wl.num_v_heads, wl.head_v_dim), float("nan"), dtype=act, device=device)
     inter = None
     if intermediates:
-        inter = torch.full((N, wl.num_v_heads, wl.head_k_dim, wl.head_v_dim), float("nan"),
-                           dtype=torch.float32, device=device)
+        tile = (wl.head_k_dim, wl.head_v_dim) if layout == "KV" else (wl.head_v_dim, wl.head_k_dim)
+        inter = torch.full((N, wl.num_v_heads) + tile, float("nan"), dtype=torch.float32,
+                           device=device)
     gdn.gdn_gating_delta_rule_update(
         d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool, d["state_idx"],
         d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq, flags=flags,
-        block_v=block_v, waves_per_group=waves_per_group, stream=stream)
+        kernel_family=kernel_family, block_v=block_v, block_k=block_k,
+        waves_per_group=waves_per_group, stream=stream, state_layout=layout)
     torch.cuda.synchronize()
     return out, inter
 
@@ -97,12 +106,14 @@ def sub_inputs(inp, seqs):
                 A_log=inp.A_log, dt_bias=inp.dt_bias, state_idx=idx, cu_seqlens=cu), rows
 
 
-def oracle_on_seqs(inp, pool0_rows, seqs, intermediates=False, no_final_writeback=False):
-    """Oracle on the sequences `seqs`; pool0_rows [len(seqs), H_v, K, V] holds
-    their initial states.  Returns (out rows, final states, inter rows, rows)."""
+def oracle_on_seqs(inp, pool0_rows, seqs, intermediates=False, no_final_writeback=False,
+                   layout="KV"):
+    """Oracle on the sequences `seqs`; pool0_rows [len(seqs), H_v, K, V] (or
+    [.., V, K] for layout "VK") holds their initial states.  Returns (out rows,
+    final states, inter rows, rows) in that layout."""
     d, rows = sub_inputs(inp, seqs)
     pool = np.ascontiguousarray(pool0_rows, dtype=np.float32).copy()
     out, inter = oracle.update(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
                                pool, d["state_idx"], d["cu_seqlens"], intermediates=intermediates,
-                               no_final_writeback=no_final_writeback)
+                               no_final_writeback=no_final_writeback, state_layout=layout)
     return out, pool, inter, rows

@@ -390,7 +390,27 @@ def pin_structure(upd):
     assert oe.shape[0] == 0 and np.array_equal(pe, pool), "empty batch"
 
 
+def pin_state_layouts(upd):
+    """The transposed storage order ("VK": K fastest) holds the same state:
+    running on the transposed pool gives the same outputs bit for bit and the
+    transposed final states and intermediates."""
+    rng = np.random.default_rng(21)
+    Hk, Hv, K, V = 2, 4, 6, 5
+    lens = [3, 1, 2]
+    d, pool, cu = _batch(rng, 3, Hk, Hv, K, V, lens, 4)
+    idx = np.array([3, -1, 0], np.int32)
+    args = (d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"])
+    p_kv = pool.copy()
+    o_kv, i_kv = upd(*args, p_kv, idx, cu, intermediates=True)
+    p_vk = np.ascontiguousarray(pool.transpose(0, 1, 3, 2))
+    o_vk, i_vk = upd(*args, p_vk, idx, cu, intermediates=True, state_layout="VK")
+    assert np.array_equal(o_kv, o_vk, equal_nan=True), "layouts give different outputs"
+    assert np.array_equal(p_vk, p_kv.transpose(0, 1, 3, 2)), "layouts give different states"
+    assert np.array_equal(i_vk, i_kv.transpose(0, 1, 3, 2), equal_nan=True)
+
+
 ALL_PINS = [pin_worked_example, pin_gamma_closed_form, pin_beta_closed_form,
             pin_unit_write, pin_write_and_orthogonal_complement,
             pin_zero_state_output, pin_eps_inside_root, pin_matrix_form,
-            pin_chain, pin_gqa_is_mha, pin_scale_invariance, pin_structure]
+            pin_chain, pin_gqa_is_mha, pin_scale_invariance, pin_structure,
+            pin_state_layouts]

@@ -96,7 +96,11 @@ def test_valid_config_passes():
     ("block_v", 12, 7),
     ("block_v", 256, 7),
     ("waves_per_group", 9, 7),
-    ("waves_per_group", 3, 7),      # does not divide G*V/BV = 8
+    ("waves_per_group", 3, 7),      # row split: not a multiple of the 4 waves per head
+    ("kernel_family", 3, 7),        # value rows need the VK layout
+    ("kernel_family", 4, 7),
+    ("state_layout", 2, 7),
+    ("block_k", 48, 7),             # no row-split kernel with 48 rows per wave
 ])
 def test_invalid_config(field, value, code):
     c = base_cfg(**{field: value})
@@ -107,6 +111,14 @@ def test_invalid_config(field, value, code):
 def test_unsupported_block_for_k():
     # K = 256 with 64-column tiles would need 256 state VGPRs per lane
     assert validate(base_cfg(head_k_dim=256, block_v=64)) == 7
+    # column tiles: waves must divide G*V/block_v = 8
+    assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES, waves_per_group=3)) == 7
+    # the row-split kernel takes one token per sequence
+    assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT, tokens_per_seq=2,
+                             num_tokens=8)) == 7
+    assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT, block_v=32)) == 7
+    # column tiles cover all K rows
+    assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES, block_k=32)) == 7
 
 
 def test_null_pointers():
@@ -169,8 +181,40 @@ def test_plan_tile_table():
     assert odd_rows.waves_per_group == 4 and odd_rows.workgroups == 4 * 2 * 3
     forced = gdn.gdn_plan(base_cfg(block_v=16, waves_per_group=4), False)
     assert forced.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
-    assert forced.block_v == 16 and forced.waves_per_group == 4
+    assert forced.block_v == 16 and forced.waves_per_group == 4 and forced.block_k == 128
     assert forced.workgroups == 4 * 2 * (2 * 8 // 4)
+    # row split, 16 rows per wavefront (8 rows per lane): 8 waves per head
+    r16 = gdn.gdn_plan(base_cfg(block_k=16), False)
+    assert r16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and r16.block_k == 16
+    assert r16.waves_per_group == 8 and r16.workgroups == 4 * 2 * 2
+    # row split, one head per workgroup
+    r1 = gdn.gdn_plan(base_cfg(waves_per_group=4), False)
+    assert r1.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and r1.block_k == 32
+    assert r1.waves_per_group == 4 and r1.workgroups == 4 * 2 * 2
+    # forcing column tiles for a single token
+    c1 = gdn.gdn_plan(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), False)
+    assert c1.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and c1.block_v == 32
+
+
+def test_plan_value_rows():
+    vk = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, num_seqs=512, num_tokens=512,
+                               num_k_heads=16, num_v_heads=32), False)
+    assert vk.kernel_family == gdn.GDN_KERNEL_VALUE_ROWS
+    assert vk.block_v == 32 and vk.block_k == 128      # 32 whole value-rows per wavefront
+    assert vk.waves_per_group == 8 and vk.workgroups == 512 * 16 and vk.lds_bytes == 0
+    multi = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, tokens_per_seq=4,
+                                  num_tokens=16), True)
+    assert multi.kernel_family == gdn.GDN_KERNEL_VALUE_ROWS and multi.multi_token == 1
+    w4 = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, waves_per_group=4), False)
+    assert w4.waves_per_group == 4 and w4.workgroups == 4 * 2 * 2
+    assert validate(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, block_v=32)) == 7
+    assert validate(base_cfg(state_layout=gdn.GDN_LAYOUT_VK,
+                             kernel_family=gdn.GDN_KERNEL_ROW_SPLIT)) == 7
+    assert validate(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, waves_per_group=3)) == 7
+    # K = V = 256: 16 wavefronts per head, spread over two 8-wave workgroups
+    big = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, head_k_dim=256,
+                                head_v_dim=256), False)
+    assert big.block_v == 16 and big.waves_per_group == 8 and big.workgroups == 4 * 2 * 4
 
 
 def test_binding_rejects_bad_tensors_on_cpu():

@@ -32,7 +32,10 @@ MUTANTS = {
                             "const double gamma = exp(0.5 * g);"),
     "sigmoid_sign": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
     "dt_bias_dropped": ("a[t * Hv + h] + dt_bias[h]", "a[t * Hv + h]"),
-    "no_writeback": ("tile[e] = (float)S[e];", "tile[e] = tile[e];"),
+    "no_writeback": ("                    tile[kk * row_stride + c * col_stride] = (float)S[(size_t)kk * V + c];",
+                     "                    tile[kk * row_stride + c * col_stride] = tile[kk * row_stride + c * col_stride];"),
+    "layout_ignored_on_load": ("S[(size_t)kk * V + c] = (double)tile[kk * row_stride + c * col_stride];",
+                               "S[(size_t)kk * V + c] = (double)tile[(size_t)kk * V + c];"),
     "intermediate_row": ("intermediate + ((size_t)t * Hv + h)",
                          "intermediate + ((size_t)(t1 - 1) * Hv + h)"),
     "varlen_end": ("cu_seqlens ? cu_seqlens[i + 1]", "cu_seqlens ? cu_seqlens[i] + 1"),

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from gpu_helpers import (TOL_STATE_GUARD, announce, live_rows, oracle_on_seqs, rel_err, run_gpu,
-                         to_np, tol_for)
+                         to_layout, to_np, tol_for)
 from linear_attention_recurrent_gating_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -23,19 +23,21 @@ def dev():
     return torch.device("cuda:0")
 
 
-def full_check(wl, dev, block_v=0, waves=0, check_inter=True):
+def full_check(wl, dev, block_v=0, waves=0, check_inter=True, family=0, block_k=0, layout="KV"):
     """Whole-batch parity: out, final states, intermediates, untouched rows."""
     import torch
     announce(f"{wl.name} B={wl.num_seqs} H={wl.num_k_heads}/{wl.num_v_heads} K={wl.head_k_dim} "
-             f"V={wl.head_v_dim} act={wl.act} bv={block_v} waves={waves}")
+             f"V={wl.head_v_dim} act={wl.act} layout={layout} family={family} bv={block_v} "
+             f"bk={block_k} waves={waves}")
     inp = W.make_host_inputs(wl)
-    pool_np = W.make_pool_host(wl)
+    pool_np = to_layout(W.make_pool_host(wl), layout)
     pool = torch.from_numpy(pool_np).to(dev)
-    out, inter = run_gpu(inp, pool, dev, block_v=block_v, waves_per_group=waves)
+    out, inter = run_gpu(inp, pool, dev, block_v=block_v, waves_per_group=waves,
+                         kernel_family=family, block_k=block_k, layout=layout)
     seqs = np.arange(wl.num_seqs)
     ref_pool_rows = pool_np[np.maximum(inp.state_idx, 0)]
     o_ref, s_ref, i_ref, rows = oracle_on_seqs(inp, ref_pool_rows, seqs,
-                                               intermediates=wl.intermediates)
+                                               intermediates=wl.intermediates, layout=layout)
     tol = tol_for(wl)
     live, dead = live_rows(inp)
     out_np = to_np(out)
@@ -98,6 +100,22 @@ def test_single_token_all_head_dims(dev, K, V):
         wl = W.Workload(f"decode_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
                         num_padded=1)
         full_check(wl, dev)
+
+
+@pytest.mark.parametrize("K,V", [(32, 32), (64, 128), (128, 32), (128, 64), (128, 128),
+                                 (256, 32), (256, 64)], ids=lambda x: str(x))
+def test_row_split_eight_rows_per_lane(dev, K, V):
+    """Row split with 8 state rows per lane (block_k = 8 * rows per
+    instruction) and with one head per workgroup."""
+    import linear_attention_recurrent_gating_amd as gdn
+    rg = 64 // (V // 4)
+    for act, seed in ((W.ACT_BF16, 63), (W.ACT_F32, 64)):
+        wl = W.Workload(f"rows8_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
+                        num_padded=1)
+        if K >= 8 * rg and K // (8 * rg) <= 8:
+            full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=8 * rg)
+        kw = max(1, K // (16 * rg))
+        full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, waves=kw)
 
 
 def test_decode_kernel_families_agree(dev):
@@ -358,3 +376,102 @@ def test_side_stream(dev):
         o2, _ = run_gpu(inp, p2, dev, tensors=d, stream=s)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(p1, p2)
+
+
+# ------------------------------------------------------------------ VK layout
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_vk_small(dev, wl):
+    full_check(wl, dev, layout="VK")
+
+
+@pytest.mark.parametrize("K,V", ROW_SPLIT_PAIRS, ids=lambda x: str(x))
+def test_vk_all_head_dims(dev, K, V):
+    """The value-row kernel over every (K, V): one token and three tokens."""
+    for act, seed, T in ((W.ACT_BF16, 70, 1), (W.ACT_F32, 71, 1), (W.ACT_BF16, 72, 3)):
+        wl = W.Workload(f"vk_k{K}_v{V}_{act}_t{T}", seed + K + V, 5, T, 2, 4, K, V, act, 8, 0.05,
+                        num_padded=1, intermediates=(T == 3))
+        full_check(wl, dev, layout="VK")
+
+
+@pytest.mark.parametrize("wl", [W.QWEN3NEXT_B64, W.SPEC_VERIFY, W.VARLEN_LONG,
+                                W.SPEC_VERIFY.with_(name="spec_verify_weak_vk", decay="weak", seed=46)],
+                         ids=lambda w: w.name)
+def test_vk_workloads(dev, wl):
+    full_check(wl, dev, layout="VK")
+
+
+@pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
+def test_vk_decode_b512_full_size_sampled(dev, wl):
+    """Full-size decode with the VK pool, 48 sampled sequences against the
+    oracle, untouched slots bitwise over the whole pool."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce(f"{wl.name} VK full size")
+    inp = W.make_host_inputs(wl)
+    pool = W.make_pool_torch(wl, dev).transpose(-1, -2).contiguous()
+    pool0 = pool.clone()
+    out, _ = run_gpu(inp, pool, dev, layout="VK")
+    rng = np.random.default_rng(98)
+    seqs = np.sort(rng.choice(wl.num_seqs, size=48, replace=False))
+    sl = torch.from_numpy(inp.state_idx[seqs]).long().to(dev)
+    o_ref, s_ref, _, rows = oracle_on_seqs(inp, pool0[sl].cpu().numpy(), seqs, layout="VK")
+    assert rel_err(to_np(out[torch.from_numpy(rows).to(dev)]), o_ref) <= tol_for(wl)
+    assert rel_err(pool[sl].cpu().numpy(), s_ref) <= TOL_STATE_GUARD
+    changed = (pool != pool0).flatten(1).any(dim=1).cpu().numpy()
+    assert set(np.nonzero(changed)[0]) <= set(inp.state_idx.tolist()), "untouched slot changed"
+    B = wl.num_seqs
+    info = gdn.gdn_plan(gdn.make_config(torch.empty(B, wl.num_k_heads, 128),
+                                        torch.empty(B, wl.num_v_heads, 128), pool,
+                                        torch.from_numpy(inp.state_idx), state_layout="VK",
+                                        tokens_per_seq=1), False)
+    assert info.kernel_family == gdn.GDN_KERNEL_VALUE_ROWS
+
+
+def test_vk_chain_bitwise(dev):
+    """With the VK layout the one-token and the multi-token calls run the same
+    per-token code: T chained one-token calls equal one T-token call bit for
+    bit, and each chained state equals the intermediate."""
+    import torch
+    announce("vk chain bitwise")
+    wl = W.Workload("vk_chain", 73, 3, 6, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05, intermediates=True)
+    inp = W.make_host_inputs(wl)
+    pool_np = to_layout(W.make_pool_host(wl), "VK")
+    pool_multi = torch.from_numpy(pool_np).to(dev)
+    out_multi, inter = run_gpu(inp, pool_multi, dev, layout="VK")
+    pool_chain = torch.from_numpy(pool_np).to(dev)
+    T = wl.tokens_per_seq
+    for t in range(T):
+        rows = np.arange(wl.num_seqs) * T + t
+        step = W.HostInputs(wl.with_(tokens_per_seq=1, intermediates=False), inp.q[rows],
+                            inp.k[rows], inp.v[rows], inp.a[rows], inp.b[rows], inp.A_log,
+                            inp.dt_bias, inp.state_idx, None, np.ones(wl.num_seqs, np.int64),
+                            {n: x[rows] for n, x in inp.bits.items()})
+        out_t, _ = run_gpu(step, pool_chain, dev, layout="VK")
+        r = torch.from_numpy(rows).to(dev)
+        assert torch.equal(out_t, out_multi[r]), f"out differs at t={t}"
+        for i in range(wl.num_seqs):
+            assert torch.equal(pool_chain[int(inp.state_idx[i])], inter[int(rows[i])])
+    assert torch.equal(pool_chain, pool_multi)
+
+
+def test_vk_matches_kv(dev):
+    """The two storage orders compute the same update (to fp32 rounding)."""
+    import torch
+    announce("vk vs kv")
+    wl = W.Workload("vk_kv", 74, 8, 5, 2, 4, 128, 128, W.ACT_F32, 10, 0.05, intermediates=True)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    p_kv = torch.from_numpy(pool_np).to(dev)
+    p_vk = torch.from_numpy(to_layout(pool_np, "VK")).to(dev)
+    o_kv, i_kv = run_gpu(inp, p_kv, dev)
+    o_vk, i_vk = run_gpu(inp, p_vk, dev, layout="VK")
+    assert rel_err(to_np(o_vk), to_np(o_kv)) <= 1e-5
+    assert rel_err(p_vk.transpose(-1, -2).cpu().numpy(), p_kv.cpu().numpy()) <= 1e-5
+    assert rel_err(i_vk.transpose(-1, -2).cpu().numpy(), i_kv.cpu().numpy()) <= 1e-5
+
+
+def test_vk_waves_override(dev):
+    import linear_attention_recurrent_gating_amd as gdn
+    for waves in (4, 8):
+        wl = W.Workload(f"vk_waves{waves}", 75, 4, 2, 2, 4, 128, 128, W.ACT_BF16, 6, 0.05)
+        full_check(wl, dev, layout="VK", waves=waves, family=gdn.GDN_KERNEL_VALUE_ROWS)
