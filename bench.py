@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for the CPU baseline (0 skips it)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the unfused pair instead: gdn_gating + gdn_recurrent_update per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead: time a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -260,8 +262,19 @@ def main():
             pool_rows0 = np.ascontiguousarray(np.swapaxes(pool_rows0, -1, -2))
 
     stream = torch.cuda.current_stream(dev)
+    g_buf = torch.empty(inp.num_tokens, wl.num_v_heads, dtype=torch.float32, device=dev)
+    beta_buf = torch.empty_like(g_buf)
 
     def step(i):
+        if args.unfused:
+            gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], g_buf, beta_buf,
+                           num_k_heads=wl.num_k_heads, stream=stream.cuda_stream)
+            gdn.gdn_recurrent_update(
+                d["q"], d["k"], d["v"], g_buf, beta_buf, pool, idx_sets[i % sets],
+                d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
+                kernel_family=args.family, block_v=args.block_v, block_k=args.block_k,
+                waves_per_group=args.waves, stream=stream.cuda_stream, state_layout=args.layout)
+            return
         gdn.gdn_gating_delta_rule_update(
             d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool,
             idx_sets[i % sets], d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
@@ -316,6 +329,8 @@ def main():
                    "slot_sets": sets, "kernel": KERNEL_NAMES[info.kernel_family],
                    "block_v": info.block_v, "block_k": info.block_k,
                    "waves_per_group": info.waves_per_group, "workgroups": info.workgroups,
+                   "gates": "unfused pair (gdn_gating + gdn_recurrent_update)" if args.unfused
+                            else "fused",
                    "parallelism": "single GPU"},
         "hbm_gb_s": achieved,
         "hbm_frac_of_peak": achieved / HBM_PEAK_GBS,

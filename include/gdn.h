@@ -102,6 +102,14 @@ typedef struct gdn_config {
                                 0 = dense (H_k*K).  Heads are dense within a token */
     int64_t k_stride_tok;    /* same for k                                       */
     int64_t v_stride_tok;    /* same for v (dense = H_v*V)                       */
+    int64_t ab_stride_tok;   /* elements between tokens of a and b; 0 = dense H_v */
+    int32_t ab_stride_khead; /* elements between the k-heads' groups of a and b;
+                                0 = dense G.  Element (t, h) of a (and of b) is
+                                read at t*ab_stride_tok + (h/G)*ab_stride_khead
+                                + h%G, which reads a and b straight out of a
+                                projection packed per k-head (vLLM PR #37975,
+                                implementation: the a/b projection is reshaped
+                                to (H_k, 2*H_v/H_k))                              */
     uint32_t flags;          /* GDN_FLAG_*                                       */
     int32_t state_layout;    /* GDN_LAYOUT_KV (0) or GDN_LAYOUT_VK (1)           */
     /* Tiling overrides (0 = the library's static table).  They change the
@@ -151,7 +159,7 @@ void gdn_default_config(gdn_config* cfg);
  *
  *  q, k     [N, H_k, K]   act_dtype; token stride q/k_stride_tok elements
  *  v        [N, H_v, V]   act_dtype; token stride v_stride_tok
- *  a, b     [N, H_v]      act_dtype, dense
+ *  a, b     [N, H_v]      act_dtype (dense, or strided per ab_stride_*)
  *  A_log, dt_bias [H_v]   fp32
  *  state_pool [num_slots, H_v, K, V] fp32 (GDN_LAYOUT_KV) or
  *             [num_slots, H_v, V, K] (GDN_LAYOUT_VK); updated in place
@@ -177,6 +185,28 @@ gdn_status gdn_gating_delta_rule_update(
     const float* A_log, const float* dt_bias, float* state_pool,
     const int32_t* state_idx, const int32_t* cu_seqlens, void* out,
     float* intermediate_states, const gdn_config* cfg, void* stream);
+
+/*
+ * The unfused pair, for callers that keep the gates as tensors (vLLM PR
+ * #35777 describes the fused op as replacing a separate gating kernel and a
+ * recurrent update that consumes its g and beta).
+ *
+ * gdn_gating: g[t,h] = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h]) and
+ * beta[t,h] = sigmoid(b[t,h]) for the cfg->num_tokens tokens (g, beta dense
+ * fp32 [N, H_v]; a, b strided as in the fused call).  Uses num_tokens,
+ * num_k_heads, num_v_heads, act_dtype and the ab strides of cfg.
+ *
+ * gdn_recurrent_update: the update of gdn_gating_delta_rule_update with
+ * gamma = exp(g) and beta taken from those tensors.  The pair gives the
+ * fused call's results bit for bit.
+ */
+gdn_status gdn_gating(const void* a, const void* b, const float* A_log, const float* dt_bias,
+                      float* g, float* beta, const gdn_config* cfg, void* stream);
+
+gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float* state_pool, const int32_t* state_idx,
+                                const int32_t* cu_seqlens, void* out, float* intermediate_states,
+                                const gdn_config* cfg, void* stream);
 
 /* Host-side argument check of gdn_gating_delta_rule_update (same arguments,
  * no stream); launches nothing and never touches device memory. */

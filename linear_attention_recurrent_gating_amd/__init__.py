@@ -36,8 +36,9 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
                 5: "GDN_ERR_MISALIGNED", 6: "GDN_ERR_LAUNCH", 7: "GDN_ERR_BAD_ARGUMENT"}
 
 # Every symbol include/gdn.h declares.
-EXPORTED = ("gdn_default_config", "gdn_gating_delta_rule_update", "gdn_validate", "gdn_plan",
-            "gdn_status_string", "gdn_last_error_message", "gdn_abi_version")
+EXPORTED = ("gdn_default_config", "gdn_gating_delta_rule_update", "gdn_gating",
+            "gdn_recurrent_update", "gdn_validate", "gdn_plan", "gdn_status_string",
+            "gdn_last_error_message", "gdn_abi_version")
 
 
 class GdnConfig(ctypes.Structure):
@@ -48,6 +49,7 @@ class GdnConfig(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("l2norm_eps", ctypes.c_float), ("q_stride_tok", ctypes.c_int64),
                 ("k_stride_tok", ctypes.c_int64), ("v_stride_tok", ctypes.c_int64),
+                ("ab_stride_tok", ctypes.c_int64), ("ab_stride_khead", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("state_layout", ctypes.c_int32),
                 ("kernel_family", ctypes.c_int32),
                 ("block_v", ctypes.c_int32), ("block_k", ctypes.c_int32),
@@ -78,6 +80,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn_default_config.restype = None
     lib.gdn_gating_delta_rule_update.argtypes = [P] * 12 + [C, P]
     lib.gdn_gating_delta_rule_update.restype = ctypes.c_int
+    lib.gdn_gating.argtypes = [P] * 6 + [C, P]
+    lib.gdn_gating.restype = ctypes.c_int
+    lib.gdn_recurrent_update.argtypes = [P] * 10 + [C, P]
+    lib.gdn_recurrent_update.restype = ctypes.c_int
     lib.gdn_validate.argtypes = [P] * 12 + [C]
     lib.gdn_validate.restype = ctypes.c_int
     lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
@@ -129,6 +135,23 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _ab_strides(a, b, N, Hv, Hk):
+    """(ab_stride_tok, ab_stride_khead) of a/b given as dense [N, H_v] tensors or
+    as [N, H_k, G] views (e.g. slices of a projection packed per k-head)."""
+    G = Hv // Hk
+    if a.shape != b.shape or a.stride() != b.stride():
+        raise ValueError("a and b must have the same shape and strides")
+    if a.dim() == 2:
+        if tuple(a.shape) != (N, Hv) or a.stride(1) != 1:
+            raise ValueError(f"a/b must be [{N}, {Hv}] with unit stride over heads")
+        return (a.stride(0) if N > 1 else 0), 0
+    if a.dim() == 3:
+        if tuple(a.shape) != (N, Hk, G) or a.stride(2) != 1:
+            raise ValueError(f"a/b views must be [{N}, {Hk}, {G}] with unit innermost stride")
+        return (a.stride(0) if N > 1 else 0), a.stride(1)
+    raise ValueError("a/b must be [N, H_v] or [N, H_k, G]")
+
+
 def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
                    intermediate_states, state_layout=GDN_LAYOUT_KV):
     """dtype/shape/device/layout checks the C-ABI cannot make on raw pointers."""
@@ -141,13 +164,15 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
     if act not in (torch.float32, torch.bfloat16):
         raise TypeError(f"activations must be float32 or bfloat16, got {act}")
     for name, t in (("k", k), ("v", v), ("a", a), ("b", b), ("out", out)):
-        if t.dtype != act:
+        if t is not None and t.dtype != act:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {act} like q")
-    for name, t, shape in (("a", a, (N, Hv)), ("b", b, (N, Hv)), ("out", out, (N, Hv, V))):
-        if tuple(t.shape) != shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {list(shape)} tensor")
+    if out is not None and (tuple(out.shape) != (N, Hv, V) or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous [{N}, {Hv}, {V}] tensor")
+    if a is not None:
+        _ab_strides(a, b, N, Hv, q.shape[1])
     for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
-        if t.dtype != torch.float32 or tuple(t.shape) != (Hv,) or not t.is_contiguous():
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (Hv,)
+                              or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous float32 [{Hv}] tensor")
     tile = (K, V) if _LAYOUTS[state_layout] == GDN_LAYOUT_KV else (V, K)
     if (state_pool.dtype != torch.float32 or state_pool.dim() != 4
@@ -179,7 +204,7 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
 def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=None,
                 scale: float = 0.0, eps: float = 1e-6, flags: int = 0, kernel_family: int = 0,
                 block_v: int = 0, block_k: int = 0, waves_per_group: int = 0,
-                k=None, state_layout=GDN_LAYOUT_KV) -> GdnConfig:
+                k=None, state_layout=GDN_LAYOUT_KV, a=None, b=None) -> GdnConfig:
     """Sizes and strides of a call, read off the tensors' shapes."""
     import torch
     N, Hk, K = q.shape
@@ -206,6 +231,8 @@ def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=
         if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
             raise ValueError("heads must be dense within a token (strides [*, D, 1])")
         setattr(cfg, name, t.stride(0) if t.shape[0] > 1 else 0)
+    if a is not None:
+        cfg.ab_stride_tok, cfg.ab_stride_khead = _ab_strides(a, b, N, Hv, Hk)
     cfg.flags = flags
     cfg.kernel_family = kernel_family
     cfg.block_v = block_v
@@ -235,7 +262,7 @@ def gdn_gating_delta_rule_update(q, k, v, a, b, A_log, dt_bias, state_pool, stat
     cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
                       scale=scale, eps=eps, flags=flags, kernel_family=kernel_family,
                       block_v=block_v, block_k=block_k, waves_per_group=waves_per_group, k=k,
-                      state_layout=state_layout)
+                      state_layout=state_layout, a=a, b=b)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -244,6 +271,80 @@ def gdn_gating_delta_rule_update(q, k, v, a, b, A_log, dt_bias, state_pool, stat
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out),
         _ptr(intermediate_states), ctypes.byref(cfg), stream))
+    return out
+
+
+def gdn_gating(a, b, A_log, dt_bias, g=None, beta=None, *, num_k_heads=None, stream=None):
+    """The standalone gating step: g = -exp(A_log)*softplus(a + dt_bias) and
+    beta = sigmoid(b), fp32 [N, H_v].  a, b: [N, H_v], or [N, H_k, G] views
+    (then num_k_heads is taken from them).  Returns (g, beta)."""
+    import torch
+    if a.dim() == 3:
+        N, Hk, G = a.shape
+        Hv = Hk * G
+    else:
+        N, Hv = a.shape
+        Hk = num_k_heads or Hv
+    if g is None:
+        g = torch.empty(N, Hv, dtype=torch.float32, device=a.device)
+    if beta is None:
+        beta = torch.empty(N, Hv, dtype=torch.float32, device=a.device)
+    for name, t in (("g", g), ("beta", beta)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (N, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [{N}, {Hv}] tensor")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (Hv,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [{Hv}] tensor")
+    if a.device.type != "cuda" or any(t.device != a.device for t in (b, A_log, dt_bias, g, beta)):
+        raise ValueError("tensors must live on one GPU")
+    cfg = gdn_default_config()
+    cfg.num_tokens = N
+    cfg.num_k_heads, cfg.num_v_heads = Hk, Hv
+    if a.dtype == torch.bfloat16:
+        cfg.act_dtype = GDN_DTYPE_BF16
+    elif a.dtype == torch.float32:
+        cfg.act_dtype = GDN_DTYPE_F32
+    else:
+        raise TypeError(f"a/b must be float32 or bfloat16, got {a.dtype}")
+    cfg.ab_stride_tok, cfg.ab_stride_khead = _ab_strides(a, b, N, Hv, Hk)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(raw_library().gdn_gating(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g),
+                                    _ptr(beta), ctypes.byref(cfg), stream))
+    return g, beta
+
+
+def gdn_recurrent_update(q, k, v, g, beta, state_pool, state_idx, cu_seqlens=None, out=None,
+                         intermediate_states=None, *, tokens_per_seq=None, scale: float = 0.0,
+                         eps: float = 1e-6, flags: int = 0, kernel_family: int = 0,
+                         block_v: int = 0, block_k: int = 0, waves_per_group: int = 0,
+                         stream=None, state_layout=GDN_LAYOUT_KV):
+    """The update with precomputed gates (g, beta: fp32 [N, H_v], e.g. from
+    gdn_gating).  Other arguments as gdn_gating_delta_rule_update."""
+    import torch
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    N, Hv = v.shape[0], v.shape[1]
+    for name, t in (("g", g), ("beta", beta)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (N, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [{N}, {Hv}] tensor")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on the same device")
+    _check_tensors(q, k, v, None, None, None, None, state_pool, state_idx, cu_seqlens, out,
+                   intermediate_states, state_layout)
+    cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
+                      scale=scale, eps=eps, flags=flags, kernel_family=kernel_family,
+                      block_v=block_v, block_k=block_k, waves_per_group=waves_per_group, k=k,
+                      state_layout=state_layout)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(raw_library().gdn_recurrent_update(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(state_idx),
+        _ptr(cu_seqlens), _ptr(out), _ptr(intermediate_states), ctypes.byref(cfg), stream))
     return out
 
 

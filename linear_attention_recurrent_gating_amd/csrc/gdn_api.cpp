@@ -257,6 +257,128 @@ gdn_status debug_check_indices(const gdn_config& c, const int32_t* state_idx,
     return GDN_OK;
 }
 
+// a/b strides: element (t, h) at t*ab_stride_tok + (h/G)*ab_stride_khead + h%G.
+gdn_status check_ab_strides(const gdn_config& c) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    if (c.ab_stride_khead != 0 && c.ab_stride_khead < G)
+        return fail(GDN_ERR_BAD_SHAPE, "ab_stride_khead = %d is below G = %d", c.ab_stride_khead, G);
+    const int64_t kh = c.ab_stride_khead ? c.ab_stride_khead : G;
+    const int64_t row = (c.num_k_heads - 1) * kh + G;
+    if (c.ab_stride_tok != 0 && c.ab_stride_tok < row)
+        return fail(GDN_ERR_BAD_SHAPE, "ab_stride_tok = %lld is below the %lld elements a token "
+                                       "of a/b spans", static_cast<long long>(c.ab_stride_tok),
+                    static_cast<long long>(row));
+    if (c.ab_stride_tok < 0) return fail(GDN_ERR_BAD_SHAPE, "ab_stride_tok < 0");
+    return GDN_OK;
+}
+
+// Arguments of the update, with either (a, b, A_log, dt_bias) or precomputed
+// (g, beta).
+gdn_status validate_update(const void* q, const void* k, const void* v, const void* a, const void* b,
+                           const float* A_log, const float* dt_bias, const float* g,
+                           const float* beta, const float* state_pool, const int32_t* state_idx,
+                           const int32_t* cu_seqlens, const void* out,
+                           const float* intermediate_states, const gdn_config* cfg) {
+    g_last_error[0] = '\0';
+    gdn_status s = check_config(cfg, cu_seqlens != nullptr);
+    if (s != GDN_OK) return s;
+    s = check_ab_strides(*cfg);
+    if (s != GDN_OK) return s;
+    if (cfg->num_seqs == 0) return GDN_OK;
+    const size_t esize = cfg->act_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    const bool pregated = g != nullptr;
+    struct { const void* p; const char* name; size_t align; } ptrs[] = {
+        {q, "q", 16}, {k, "k", 16}, {v, "v", 16},
+        {pregated ? g : a, pregated ? "g" : "a", pregated ? 4 : esize},
+        {pregated ? beta : b, pregated ? "beta" : "b", pregated ? 4 : esize},
+        {pregated ? g : A_log, pregated ? "g" : "A_log", 4},
+        {pregated ? beta : dt_bias, pregated ? "beta" : "dt_bias", 4},
+        {state_pool, "state_pool", 16}, {state_idx, "state_idx", 4}, {out, "out", 16}};
+    for (const auto& e : ptrs) {
+        if (!e.p) return fail(GDN_ERR_NULL_POINTER, "%s is NULL", e.name);
+        if (!aligned(e.p, e.align))
+            return fail(GDN_ERR_MISALIGNED, "%s is not %zu-byte aligned", e.name, e.align);
+    }
+    if (cu_seqlens && !aligned(cu_seqlens, 4))
+        return fail(GDN_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
+    if (intermediate_states && !aligned(intermediate_states, 16))
+        return fail(GDN_ERR_MISALIGNED, "intermediate_states is not 16-byte aligned");
+    return GDN_OK;
+}
+
+gdn_status run_update(const void* q, const void* k, const void* v, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, const float* g, const float* beta,
+                      float* state_pool, const int32_t* state_idx, const int32_t* cu_seqlens,
+                      void* out, float* intermediate_states, const gdn_config* cfg, void* stream) {
+    gdn_status s = validate_update(q, k, v, a, b, A_log, dt_bias, g, beta, state_pool, state_idx,
+                                   cu_seqlens, out, intermediate_states, cfg);
+    if (s != GDN_OK) return s;
+    const gdn_config& c = *cfg;
+    if (c.num_seqs == 0) return GDN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c.flags & GDN_FLAG_DEBUG_CHECKS) {
+        s = debug_check_indices(c, state_idx, cu_seqlens, st);
+        if (s != GDN_OK) return s;
+    }
+    const bool has_cu = cu_seqlens != nullptr;
+    gdn::LaunchShape sh{};
+    s = plan_launch(c, has_cu, sh);
+    if (s != GDN_OK) return s;
+
+    gdn::FusedParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = a;
+    p.b = b;
+    p.g = g;
+    p.beta = beta;
+    p.A_log = A_log;
+    p.dt_bias = dt_bias;
+    p.pool = state_pool;
+    p.state_idx = state_idx;
+    p.cu_seqlens = cu_seqlens;
+    p.out = out;
+    p.inter = intermediate_states;
+    const int G = c.num_v_heads / c.num_k_heads;
+    const int64_t qk_dense = static_cast<int64_t>(c.num_k_heads) * c.head_k_dim;
+    p.q_stride = c.q_stride_tok ? c.q_stride_tok : qk_dense;
+    p.k_stride = c.k_stride_tok ? c.k_stride_tok : qk_dense;
+    p.v_stride = c.v_stride_tok ? c.v_stride_tok : static_cast<int64_t>(c.num_v_heads) * c.head_v_dim;
+    p.ab_stride = c.ab_stride_tok ? c.ab_stride_tok : c.num_v_heads;
+    p.ab_khead = c.ab_stride_khead ? c.ab_stride_khead : G;
+    p.T = has_cu ? 0 : c.tokens_per_seq;
+    p.Hk = c.num_k_heads;
+    p.Hv = c.num_v_heads;
+    p.G = G;
+    p.V = c.head_v_dim;
+    p.groups_per_khead =
+        static_cast<int32_t>(sh.groups / (static_cast<int64_t>(c.num_seqs) * c.num_k_heads));
+    p.scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt(static_cast<float>(c.head_k_dim));
+    p.eps = c.l2norm_eps;
+    p.write_final = (c.flags & GDN_FLAG_NO_FINAL_WRITEBACK) ? 0 : 1;
+
+    static const bool log = [] {
+        const char* e = std::getenv("GDN_LOG");
+        return e && e[0] == '1';
+    }();
+    if (log)
+        std::fprintf(stderr,
+                     "[gdn] %s K=%d V=%d act=%s gates=%s multi_token=%d block_v=%d block_k=%d "
+                     "waves=%d chunk=%d groups=%lld lds=%d\n",
+                     sh.kind == gdn::kKindRows        ? "rows"
+                     : sh.kind == gdn::kKindValueRows ? "value-rows"
+                                                      : "columns",
+                     sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", g ? "precomputed" : "fused",
+                     sh.multi_token, sh.block_v, sh.block_k, sh.waves, sh.chunk,
+                     static_cast<long long>(sh.groups), sh.lds_bytes);
+
+    const hipError_t e = gdn::launch_fused(sh, p, st);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,25 +396,8 @@ gdn_status gdn_validate(const void* q, const void* k, const void* v, const void*
                         const float* A_log, const float* dt_bias, const float* state_pool,
                         const int32_t* state_idx, const int32_t* cu_seqlens, const void* out,
                         const float* intermediate_states, const gdn_config* cfg) {
-    g_last_error[0] = '\0';
-    gdn_status s = check_config(cfg, cu_seqlens != nullptr);
-    if (s != GDN_OK) return s;
-    if (cfg->num_seqs == 0) return GDN_OK;
-    const size_t esize = cfg->act_dtype == GDN_DTYPE_F32 ? 4 : 2;
-    struct { const void* p; const char* name; size_t align; } ptrs[] = {
-        {q, "q", 16}, {k, "k", 16}, {v, "v", 16}, {a, "a", esize}, {b, "b", esize},
-        {A_log, "A_log", 4}, {dt_bias, "dt_bias", 4}, {state_pool, "state_pool", 16},
-        {state_idx, "state_idx", 4}, {out, "out", 16}};
-    for (const auto& e : ptrs) {
-        if (!e.p) return fail(GDN_ERR_NULL_POINTER, "%s is NULL", e.name);
-        if (!aligned(e.p, e.align))
-            return fail(GDN_ERR_MISALIGNED, "%s is not %zu-byte aligned", e.name, e.align);
-    }
-    if (cu_seqlens && !aligned(cu_seqlens, 4))
-        return fail(GDN_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
-    if (intermediate_states && !aligned(intermediate_states, 16))
-        return fail(GDN_ERR_MISALIGNED, "intermediate_states is not 16-byte aligned");
-    return GDN_OK;
+    return validate_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
+                           cu_seqlens, out, intermediate_states, cfg);
 }
 
 gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* info) {
@@ -323,64 +428,52 @@ gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void
                                         const int32_t* cu_seqlens, void* out,
                                         float* intermediate_states, const gdn_config* cfg,
                                         void* stream) {
-    gdn_status s = gdn_validate(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens,
-                                out, intermediate_states, cfg);
-    if (s != GDN_OK) return s;
-    const gdn_config& c = *cfg;
-    if (c.num_seqs == 0) return GDN_OK;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (c.flags & GDN_FLAG_DEBUG_CHECKS) {
-        s = debug_check_indices(c, state_idx, cu_seqlens, st);
-        if (s != GDN_OK) return s;
+    return run_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
+                      cu_seqlens, out, intermediate_states, cfg, stream);
+}
+
+gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float* state_pool, const int32_t* state_idx,
+                                const int32_t* cu_seqlens, void* out, float* intermediate_states,
+                                const gdn_config* cfg, void* stream) {
+    g_last_error[0] = '\0';
+    if (!g || !beta) {
+        if (cfg && cfg->num_seqs == 0) return GDN_OK;
+        return fail(GDN_ERR_NULL_POINTER, "g and beta must not be NULL");
     }
-    const bool has_cu = cu_seqlens != nullptr;
-    gdn::LaunchShape sh{};
-    s = plan_launch(c, has_cu, sh);
+    return run_update(q, k, v, nullptr, nullptr, nullptr, nullptr, g, beta, state_pool, state_idx,
+                      cu_seqlens, out, intermediate_states, cfg, stream);
+}
+
+gdn_status gdn_gating(const void* a, const void* b, const float* A_log, const float* dt_bias,
+                      float* g, float* beta, const gdn_config* cfg, void* stream) {
+    g_last_error[0] = '\0';
+    if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
+    const gdn_config& c = *cfg;
+    if (c.num_tokens < 0) return fail(GDN_ERR_BAD_SHAPE, "num_tokens < 0");
+    if (c.num_k_heads < 1 || c.num_v_heads < 1 || c.num_v_heads % c.num_k_heads != 0)
+        return fail(GDN_ERR_BAD_SHAPE, "H_v = %d must be a positive multiple of H_k = %d",
+                    c.num_v_heads, c.num_k_heads);
+    if (c.act_dtype != GDN_DTYPE_F32 && c.act_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_UNSUPPORTED_DTYPE, "act_dtype %d is neither F32 nor BF16", c.act_dtype);
+    gdn_status s = check_ab_strides(c);
     if (s != GDN_OK) return s;
-
-    gdn::FusedParams p{};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.a = a;
-    p.b = b;
-    p.A_log = A_log;
-    p.dt_bias = dt_bias;
-    p.pool = state_pool;
-    p.state_idx = state_idx;
-    p.cu_seqlens = cu_seqlens;
-    p.out = out;
-    p.inter = intermediate_states;
-    const int64_t qk_dense = static_cast<int64_t>(c.num_k_heads) * c.head_k_dim;
-    p.q_stride = c.q_stride_tok ? c.q_stride_tok : qk_dense;
-    p.k_stride = c.k_stride_tok ? c.k_stride_tok : qk_dense;
-    p.v_stride = c.v_stride_tok ? c.v_stride_tok : static_cast<int64_t>(c.num_v_heads) * c.head_v_dim;
-    p.T = has_cu ? 0 : c.tokens_per_seq;
-    p.Hk = c.num_k_heads;
-    p.Hv = c.num_v_heads;
-    p.G = c.num_v_heads / c.num_k_heads;
-    p.V = c.head_v_dim;
-    p.groups_per_khead = static_cast<int32_t>(sh.groups / (static_cast<int64_t>(c.num_seqs) * c.num_k_heads));
-    p.scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt(static_cast<float>(c.head_k_dim));
-    p.eps = c.l2norm_eps;
-    p.write_final = (c.flags & GDN_FLAG_NO_FINAL_WRITEBACK) ? 0 : 1;
-
-    static const bool log = [] {
-        const char* e = std::getenv("GDN_LOG");
-        return e && e[0] == '1';
-    }();
-    if (log)
-        std::fprintf(stderr,
-                     "[gdn] %s K=%d V=%d act=%s multi_token=%d block_v=%d block_k=%d waves=%d "
-                     "chunk=%d groups=%lld lds=%d\n",
-                     sh.kind == gdn::kKindRows ? "rows" : sh.kind == gdn::kKindValueRows ? "value-rows" : "columns",
-                     sh.K, c.head_v_dim,
-                     sh.act ? "bf16" : "f32", sh.multi_token, sh.block_v, sh.block_k,
-                     sh.waves, sh.chunk, static_cast<long long>(sh.groups), sh.lds_bytes);
-
-    const hipError_t e = gdn::launch_fused(sh, p, st);
-    if (e != hipSuccess)
-        return fail(GDN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    if (c.num_tokens == 0) return GDN_OK;
+    const size_t esize = c.act_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    struct { const void* p; const char* name; size_t align; } ptrs[] = {
+        {a, "a", esize}, {b, "b", esize}, {A_log, "A_log", 4}, {dt_bias, "dt_bias", 4},
+        {g, "g", 4}, {beta, "beta", 4}};
+    for (const auto& e : ptrs) {
+        if (!e.p) return fail(GDN_ERR_NULL_POINTER, "%s is NULL", e.name);
+        if (!aligned(e.p, e.align))
+            return fail(GDN_ERR_MISALIGNED, "%s is not %zu-byte aligned", e.name, e.align);
+    }
+    const int G = c.num_v_heads / c.num_k_heads;
+    const hipError_t e = gdn::launch_gating(
+        a, b, A_log, dt_bias, g, beta, c.num_tokens * c.num_v_heads, c.num_v_heads, G,
+        c.ab_stride_tok ? c.ab_stride_tok : c.num_v_heads, c.ab_stride_khead ? c.ab_stride_khead : G,
+        c.act_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(GDN_ERR_LAUNCH, "gating launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
 }
 

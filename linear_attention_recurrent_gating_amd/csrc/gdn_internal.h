@@ -15,6 +15,8 @@ struct FusedParams {
     const void* v;
     const void* a;
     const void* b;
+    const float* g;             // precomputed log-decay [N, H_v] (unfused pair) or nullptr
+    const float* beta;          // precomputed beta [N, H_v] (with g)
     const float* A_log;
     const float* dt_bias;
     float* pool;
@@ -25,6 +27,8 @@ struct FusedParams {
     int64_t q_stride;           // elements between tokens
     int64_t k_stride;
     int64_t v_stride;
+    int64_t ab_stride;          // elements between tokens of a and b
+    int32_t ab_khead;           // elements between k-heads of a and b (dense: G)
     int32_t T;
     int32_t Hk;
     int32_t Hv;
@@ -71,6 +75,11 @@ int rows_per_wave(int K, int V, int rpl_max);
 // Value-rows per wavefront of the VK-layout kernel for (K, V); 0 if there is
 // no instance for that pair.
 int vk_rows_per_wave(int K, int V);
+
+// Enqueues the standalone gating kernel (n = N*H_v outputs).
+hipError_t launch_gating(const void* a, const void* b, const float* A_log, const float* dt_bias,
+                         float* g, float* beta, int64_t n, int Hv, int G, int64_t ab_stride,
+                         int32_t ab_khead, int act, hipStream_t stream);
 
 // Enqueues the fused kernel; returns the HIP launch status.
 hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);

@@ -220,14 +220,36 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ----------------------------------------------------------------- the gates
-// gamma = exp(-exp(A_log) * softplus(a + dt_bias)), beta = sigmoid(b).
+// g = -exp(A_log) * softplus(a + dt_bias) (the log-decay), beta = sigmoid(b).
 // softplus returns x itself above 20, where log1p(exp(x)) - x < 2.1e-9.
-__device__ __forceinline__ void gates(float a, float b, float A_log, float dt_bias,
-                                      float& gamma, float& beta) {
+__device__ __forceinline__ void gate_values(float a, float b, float A_log, float dt_bias,
+                                            float& g, float& beta) {
     const float x = a + dt_bias;
     const float sp = x > 20.0f ? x : log1pf(expf(x));
-    gamma = expf(-expf(A_log) * sp);
+    g = -expf(A_log) * sp;
     beta = 1.0f / (1.0f + expf(-b));
+}
+
+// The decay factor gamma = exp(g) and beta of token t, v-head h: computed from
+// a and b (element t*ab_stride + (h/G)*ab_khead + h%G, which also reads a/b
+// packed per k-head), or taken from precomputed g and beta ([N, H_v] fp32,
+// the unfused pair).  Both routes round identically: gamma is exp of the same
+// fp32 g.
+// A_log and dt_bias are read only on the fused route (they may be null with
+// precomputed gates).
+template <int ACT>
+__device__ __forceinline__ void token_gates(const FusedParams& p, int64_t t, int h, float& gamma,
+                                            float& beta) {
+    float g;
+    if (p.g) {
+        g = p.g[t * p.Hv + h];
+        beta = p.beta[t * p.Hv + h];
+    } else {
+        const int64_t e = t * p.ab_stride + static_cast<int64_t>(h / p.G) * p.ab_khead + h % p.G;
+        gate_values(load_scalar<ACT>(p.a, e), load_scalar<ACT>(p.b, e), p.A_log[h], p.dt_bias[h],
+                    g, beta);
+    }
+    gamma = expf(g);
 }
 
 // ----------------------------------------------------------- q/k staging
@@ -334,8 +356,6 @@ gdn_fused_update(const FusedParams p) {
     for (int i = 0; i < RPL; ++i)
         S[i] = load_state(tile_r, lane_bytes, i * row_step);
 
-    const float A_log = p.A_log[h];
-    const float dt_bias = p.dt_bias[h];
 
     for (int64_t c0 = t0; c0 < t1; c0 += CHUNK) {
         const int nt = static_cast<int>(t1 - c0 < CHUNK ? t1 - c0 : CHUNK);
@@ -350,15 +370,12 @@ gdn_fused_update(const FusedParams p) {
         float4 vdirect = make_float4(0.f, 0.f, 0.f, 0.f);
         float* vs = lds + 2 * CHUNK * K + wave * (CHUNK * BV);   // [CHUNK][BV] (CHUNK > 1)
         if constexpr (CHUNK == 1) {
-            gates(load_scalar<ACT>(p.a, c0 * p.Hv + h), load_scalar<ACT>(p.b, c0 * p.Hv + h),
-                  A_log, dt_bias, gam, bet);
+            token_gates<ACT>(p, c0, h, gam, bet);
             float vv[4];
             load_act<ACT, 4>(p.v, c0 * p.v_stride + static_cast<int64_t>(h) * p.V + col, vv);
             vdirect = make_float4(vv[0], vv[1], vv[2], vv[3]);
         } else {
-            if (lane < nt)
-                gates(load_scalar<ACT>(p.a, (c0 + lane) * p.Hv + h),
-                      load_scalar<ACT>(p.b, (c0 + lane) * p.Hv + h), A_log, dt_bias, gam, bet);
+            if (lane < nt) token_gates<ACT>(p, c0 + lane, h, gam, bet);
             // v rows of this wave's tile: RG tokens per pass, LPR lanes per token
             const int tcol = col - (unit % nvb) * BV;    // column within the tile
             for (int tok = rg; tok < nt; tok += RG) {
@@ -549,10 +566,8 @@ gdn_decode_rows(const FusedParams p) {
     // while the state tile is still streaming in.
     SingleTokenQK<K, ACT> qk;
     qk.load(p, j, t, wave, lane);
-    const float a_t = load_scalar<ACT>(p.a, t * p.Hv + h);
-    const float b_t = load_scalar<ACT>(p.b, t * p.Hv + h);
-    const float A_log = p.A_log[h];
-    const float dt_bias = p.dt_bias[h];
+    float gamma, beta;
+    token_gates<ACT>(p, t, h, gamma, beta);
     float vv[4];
     load_act<ACT, 4>(p.v, t * p.v_stride + static_cast<int64_t>(h) * V + col, vv);
 
@@ -565,9 +580,6 @@ gdn_decode_rows(const FusedParams p) {
     float4 S[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) S[i] = load_state(tile_r, lane_bytes, i * row_step);
-
-    float gamma, beta;
-    gates(a_t, b_t, A_log, dt_bias, gamma, beta);
 
     // rows kw*RPW + RG*i + rg of the head sit at kw*RPW + rg*RPL + i
     qk.finish(p, qs, ks, lane, [](int kappa) {
@@ -777,10 +789,8 @@ gdn_vk_decode(const FusedParams p) {
     float qx[8], kx[8];
     load_keys<K, ACT, LPR>(p.q, t * p.q_stride + static_cast<int64_t>(pl.j) * K, c, qx);
     load_keys<K, ACT, LPR>(p.k, t * p.k_stride + static_cast<int64_t>(pl.j) * K, c, kx);
-    const float a_t = load_scalar<ACT>(p.a, t * p.Hv + h);
-    const float b_t = load_scalar<ACT>(p.b, t * p.Hv + h);
-    const float A_log = p.A_log[h];
-    const float dt_bias = p.dt_bias[h];
+    float gamma, beta;
+    token_gates<ACT>(p, t, h, gamma, beta);
     float vv[RPL];
     const int64_t vbase = t * p.v_stride + static_cast<int64_t>(h) * V + row0;
 #pragma unroll
@@ -799,8 +809,6 @@ gdn_vk_decode(const FusedParams p) {
 
     float qh[8], kh[8], kq;
     normalize_keys<LPR>(qx, kx, p.scale, p.eps, qh, kh, kq);
-    float gamma, beta;
-    gates(a_t, b_t, A_log, dt_bias, gamma, beta);
 
     const int64_t obase = (t * p.Hv + h) * static_cast<int64_t>(V) + row0;
 #pragma unroll
@@ -889,16 +897,12 @@ gdn_vk_multi(const FusedParams p) {
         for (int hh = 0; hh < 2; ++hh)
             S[i][hh] = load_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF);
 
-    const float A_log = p.A_log[h];
-    const float dt_bias = p.dt_bias[h];
 
     for (int64_t c0 = t0; c0 < t1; c0 += CHUNK) {
         const int nt = static_cast<int>(t1 - c0 < CHUNK ? t1 - c0 : CHUNK);
         stage_raw_qk<K, ACT>(p, qs, ks, pl.j, c0, nt, threadIdx.x, blockDim.x);
         float gam = 1.0f, bet = 0.0f;   // lane tau holds token tau's gates
-        if (lane < nt)
-            gates(load_scalar<ACT>(p.a, (c0 + lane) * p.Hv + h),
-                  load_scalar<ACT>(p.b, (c0 + lane) * p.Hv + h), A_log, dt_bias, gam, bet);
+        if (lane < nt) token_gates<ACT>(p, c0 + lane, h, gam, bet);
         // v of this wave's rows, permuted so lane (rg, i) reads rg*RPL + i
         for (int e = lane; e < nt * RPW; e += kWave) {
             const int tok = e / RPW, r = e % RPW;
@@ -947,6 +951,28 @@ gdn_vk_multi(const FusedParams p) {
             for (int hh = 0; hh < 2; ++hh)
                 store_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
     }
+}
+
+
+// ---------------------------------------------------------- gating kernel
+// The standalone gating step of the unfused pair (vLLM PR #35777,
+// implementation section: the gating kernel that the fused op absorbs):
+// g = -exp(A_log)*softplus(a + dt_bias) and beta = sigmoid(b), written as
+// fp32 [N, H_v].  One thread per (token, v-head).
+template <int ACT>
+__global__ void __launch_bounds__(256)
+gdn_gating_kernel(const void* a, const void* b, const float* A_log, const float* dt_bias,
+                  float* g, float* beta, int64_t n, int Hv, int G, int64_t ab_stride,
+                  int32_t ab_khead) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (e >= n) return;
+    const int64_t t = e / Hv;
+    const int h = static_cast<int>(e % Hv);
+    const int64_t src = t * ab_stride + static_cast<int64_t>(h / G) * ab_khead + h % G;
+    float gv, bv;
+    gate_values(load_scalar<ACT>(a, src), load_scalar<ACT>(b, src), A_log[h], dt_bias[h], gv, bv);
+    g[e] = gv;
+    beta[e] = bv;
 }
 
 // ------------------------------------------------------------ instance table
@@ -1100,6 +1126,18 @@ int lds_bytes_for(const LaunchShape& s, int V) {
     if (s.kind == kKindValueRows)                             // single token: no LDS at all
         floats = s.multi_token ? 2 * s.chunk * s.K + s.waves * s.chunk * s.block_v : 0;
     return floats * static_cast<int>(sizeof(float));
+}
+
+hipError_t launch_gating(const void* a, const void* b, const float* A_log, const float* dt_bias,
+                         float* g, float* beta, int64_t n, int Hv, int G, int64_t ab_stride,
+                         int32_t ab_khead, int act, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+    void* fn = act ? reinterpret_cast<void*>(&gdn_gating_kernel<1>)
+                   : reinterpret_cast<void*>(&gdn_gating_kernel<0>);
+    void* args[] = {const_cast<void**>(&a), const_cast<void**>(&b), const_cast<float**>(&A_log),
+                    const_cast<float**>(&dt_bias), &g, &beta, &n, &Hv, &G, &ab_stride, &ab_khead};
+    return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, stream);
 }
 
 hipError_t launch_fused(const LaunchShape& s, const FusedParams& p, hipStream_t stream) {

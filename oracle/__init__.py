@@ -48,6 +48,9 @@ def _load(path: str = _LIB):
                       ctypes.c_int64, ctypes.c_double, ctypes.c_double,
                       ctypes.c_int, ctypes.c_int, ctypes.c_int]
         f.restype = ctypes.c_int
+        fg = lib.gdn_oracle_gating
+        fg.argtypes = [P] * 6 + [ctypes.c_int64, ctypes.c_int]
+        fg.restype = ctypes.c_int
         _libs[path] = lib
     return lib
 
@@ -98,6 +101,26 @@ def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out, inter
+
+
+def gating(a, b, A_log, dt_bias, lib_path: str = _LIB):
+    """The standalone gating step: returns (g, beta) as float64 [N, H_v]."""
+    lib = _load(lib_path)
+    d = np.float64
+    a = np.ascontiguousarray(a, dtype=d)
+    b = np.ascontiguousarray(b, dtype=d)
+    A_log = np.ascontiguousarray(A_log, dtype=d)
+    dt_bias = np.ascontiguousarray(dt_bias, dtype=d)
+    N, Hv = a.shape
+    if b.shape != a.shape or A_log.shape != (Hv,) or dt_bias.shape != (Hv,):
+        raise ValueError("inconsistent gate shapes")
+    g = np.full((N, Hv), np.nan)
+    beta = np.full((N, Hv), np.nan)
+    rc = lib.gdn_oracle_gating(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
+                               N, Hv)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return g, beta
 
 
 def run_inputs(inp, pool: np.ndarray, scale: float = 0.0, eps: float = 1e-6,

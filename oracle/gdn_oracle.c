@@ -216,4 +216,26 @@ int gdn_oracle_update(const double *q, const double *k, const double *v,
     return status;
 }
 
+/*
+ * The gating step on its own (the kernel the fused op absorbs):
+ * g[t,h] = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h]), beta[t,h] =
+ * sigmoid(b[t,h]); a, b, g, beta dense [N, Hv].
+ */
+int gdn_oracle_gating(const double *a, const double *b, const double *A_log,
+                      const double *dt_bias, double *g, double *beta,
+                      int64_t N, int Hv)
+{
+    if (N < 0 || Hv <= 0)
+        return ORACLE_ERR_ARG;
+    if (N > 0 && (!a || !b || !A_log || !dt_bias || !g || !beta))
+        return ORACLE_ERR_ARG;
+    for (int64_t t = 0; t < N; ++t)
+        for (int h = 0; h < Hv; ++h) {
+            const int64_t e = t * Hv + h;
+            g[e] = -exp(A_log[h]) * oracle_softplus(a[e] + dt_bias[h]);
+            beta[e] = oracle_sigmoid(b[e]);
+        }
+    return ORACLE_OK;
+}
+
 int gdn_oracle_abi_version(void) { return 1; }

@@ -409,8 +409,25 @@ def pin_state_layouts(upd):
     assert np.array_equal(i_vk, i_kv.transpose(0, 1, 3, 2), equal_nan=True)
 
 
+def pin_gating_step(upd):
+    """The standalone gating step: exp(g) = (1 + e^x)^(-e^A_log) and beta is the
+    logistic of b, per (token, head), over both tails of softplus."""
+    import functools
+    import oracle
+    lib = getattr(upd, "keywords", {}).get("lib_path")
+    gate = functools.partial(oracle.gating, lib_path=lib) if lib else oracle.gating
+    xs = np.array([[-30.0, -1.0, 0.0, 0.5], [3.0, 25.0, -5.0, 0.0]])
+    A_log = np.array([0.3, np.log(2.0), -0.7, 2.5])
+    dt = np.array([0.1, -0.2, 0.3, 0.0])
+    bs = np.array([[-40.0, 0.0, np.log(3.0), 2.0], [30.0, -2.0, 1.5, -0.5]])
+    g, beta = gate(xs - dt, bs, A_log, dt)
+    _close(np.exp(g), gamma_closed_form(A_log[None, :], xs), 1e-13, "gating step: exp(g)")
+    _close(beta, beta_closed_form(bs), 1e-14, "gating step: beta")
+    assert abs(np.exp(g[0, 2]) - 0.5 ** np.exp(-0.7)) < 1e-15  # x = 0: (1+1)^(-A)
+
+
 ALL_PINS = [pin_worked_example, pin_gamma_closed_form, pin_beta_closed_form,
             pin_unit_write, pin_write_and_orthogonal_complement,
             pin_zero_state_output, pin_eps_inside_root, pin_matrix_form,
             pin_chain, pin_gqa_is_mha, pin_scale_invariance, pin_structure,
-            pin_state_layouts]
+            pin_state_layouts, pin_gating_step]

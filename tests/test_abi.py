@@ -217,6 +217,20 @@ def test_plan_value_rows():
     assert big.block_v == 16 and big.waves_per_group == 8 and big.workgroups == 4 * 2 * 4
 
 
+def test_ab_stride_validation():
+    assert validate(base_cfg(ab_stride_khead=1)) == 2            # below G = 2
+    assert validate(base_cfg(ab_stride_khead=4, ab_stride_tok=5)) == 2   # below (H_k-1)*4 + 2 = 6
+    assert validate(base_cfg(ab_stride_khead=4, ab_stride_tok=8)) == 0
+    lib = gdn.raw_library()
+    c = base_cfg(ab_stride_khead=1)
+    assert lib.gdn_gating(A[0], A[1], A[2], A[3], A[4], A[5], ctypes.byref(c), None) == 2
+    c = base_cfg()
+    assert lib.gdn_gating(A[0], None, A[2], A[3], A[4], A[5], ctypes.byref(c), None) == 1
+    assert lib.gdn_gating(A[0], A[1], A[2], A[3], A[4] + 2, A[5], ctypes.byref(c), None) == 5
+    assert lib.gdn_recurrent_update(A[0], A[1], A[2], None, A[4], A[5], A[6], None, A[7], None,
+                                    ctypes.byref(c), None) == 1
+
+
 def test_binding_rejects_bad_tensors_on_cpu():
     import torch
     q = torch.zeros(2, 1, 32)

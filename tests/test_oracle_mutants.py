@@ -36,6 +36,9 @@ MUTANTS = {
                      "                    tile[kk * row_stride + c * col_stride] = tile[kk * row_stride + c * col_stride];"),
     "layout_ignored_on_load": ("S[(size_t)kk * V + c] = (double)tile[kk * row_stride + c * col_stride];",
                                "S[(size_t)kk * V + c] = (double)tile[(size_t)kk * V + c];"),
+    "gating_head_index": ("g[e] = -exp(A_log[h]) * oracle_softplus(a[e] + dt_bias[h]);",
+                          "g[e] = -exp(A_log[0]) * oracle_softplus(a[e] + dt_bias[h]);"),
+    "gating_beta_from_a": ("beta[e] = oracle_sigmoid(b[e]);", "beta[e] = oracle_sigmoid(a[e]);"),
     "intermediate_row": ("intermediate + ((size_t)t * Hv + h)",
                          "intermediate + ((size_t)(t1 - 1) * Hv + h)"),
     "varlen_end": ("cu_seqlens ? cu_seqlens[i + 1]", "cu_seqlens ? cu_seqlens[i] + 1"),

@@ -475,3 +475,93 @@ def test_vk_waves_override(dev):
     for waves in (4, 8):
         wl = W.Workload(f"vk_waves{waves}", 75, 4, 2, 2, 4, 128, 128, W.ACT_BF16, 6, 0.05)
         full_check(wl, dev, layout="VK", waves=waves, family=gdn.GDN_KERNEL_VALUE_ROWS)
+
+
+# ------------------------------------------------- unfused pair, packed a/b
+@pytest.mark.parametrize("act", [W.ACT_F32, W.ACT_BF16])
+def test_gating_step_vs_oracle(dev, act):
+    import torch
+    import oracle
+    import linear_attention_recurrent_gating_amd as gdn
+    announce(f"gating step {act}")
+    wl = W.Workload("gating", 80, 40, 3, 4, 8, 64, 64, act, 50, 0.05)
+    inp = W.make_host_inputs(wl)
+    d = W.to_torch(inp, dev)
+    a2 = d["a"].view(inp.num_tokens, -1)
+    g, beta = gdn.gdn_gating(a2, d["b"].view(inp.num_tokens, -1), d["A_log"], d["dt_bias"],
+                             num_k_heads=wl.num_k_heads)
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gating(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    assert rel_err(np.exp(g.cpu().numpy().astype(np.float64)), np.exp(g_ref)) <= 1e-5
+    assert rel_err(g.cpu().numpy(), g_ref) <= 1e-5
+    assert rel_err(beta.cpu().numpy(), b_ref) <= 1e-5
+
+
+UNFUSED_CASES = [
+    ("KV", W.Workload("unf_decode", 81, 9, 1, 4, 8, 128, 128, W.ACT_BF16, 12, 0.05, num_padded=2)),
+    ("KV", W.Workload("unf_spec", 82, 6, 1, 4, 8, 128, 128, W.ACT_BF16, 8, 0.05, varlen=True,
+                      len_range=(1, 20), num_padded=1, intermediates=True)),
+    ("VK", W.Workload("unf_decode_vk", 83, 9, 1, 4, 8, 128, 128, W.ACT_F32, 12, 0.05)),
+    ("VK", W.Workload("unf_multi_vk", 84, 4, 5, 2, 4, 64, 128, W.ACT_BF16, 6, 0.05,
+                      intermediates=True)),
+]
+
+
+@pytest.mark.parametrize("layout,wl", UNFUSED_CASES, ids=lambda x: x if isinstance(x, str) else x.name)
+def test_unfused_pair_equals_fused(dev, layout, wl):
+    """gdn_gating followed by gdn_recurrent_update gives the fused call's
+    results bit for bit (gamma = exp of the same fp32 g)."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce(f"unfused pair {wl.name} {layout}")
+    inp = W.make_host_inputs(wl)
+    d = W.to_torch(inp, dev)
+    pool_np = to_layout(W.make_pool_host(wl), layout)
+    p_fused = torch.from_numpy(pool_np).to(dev)
+    o_fused, i_fused = run_gpu(inp, p_fused, dev, tensors=d, layout=layout)
+    p_pair = torch.from_numpy(pool_np).to(dev)
+    N = inp.num_tokens
+    g, beta = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], num_k_heads=wl.num_k_heads)
+    out = torch.full_like(o_fused, float("nan"))
+    inter = None if i_fused is None else torch.full_like(i_fused, float("nan"))
+    gdn.gdn_recurrent_update(d["q"], d["k"], d["v"], g, beta, p_pair, d["state_idx"],
+                             d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
+                             state_layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out.nan_to_num(), o_fused.nan_to_num())
+    assert torch.equal(p_pair, p_fused)
+    if inter is not None:
+        assert torch.equal(inter.nan_to_num(), i_fused.nan_to_num())
+    assert N == g.shape[0]
+
+
+@pytest.mark.parametrize("layout", ["KV", "VK"])
+def test_packed_mixed_ba(dev, layout):
+    """a and b read straight out of a projection packed per k-head as
+    [N, H_k, 2G] (the G b-values, then the G a-values of the group) give the
+    dense result bit for bit, for the fused call and for the gating step."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce(f"packed mixed_ba {layout}")
+    wl = W.Workload("mixed_ba", 85, 7, 2, 4, 12, 64, 64, W.ACT_BF16, 9, 0.05)
+    inp = W.make_host_inputs(wl)
+    d = W.to_torch(inp, dev)
+    pool_np = to_layout(W.make_pool_host(wl), layout)
+    p_dense = torch.from_numpy(pool_np).to(dev)
+    o_dense, _ = run_gpu(inp, p_dense, dev, tensors=d, layout=layout)
+    N, Hk, G = inp.num_tokens, wl.num_k_heads, wl.group
+    mixed = torch.empty(N, Hk, 2 * G, dtype=torch.bfloat16, device=dev)
+    mixed[:, :, :G] = d["b"].view(N, Hk, G)
+    mixed[:, :, G:] = d["a"].view(N, Hk, G)
+    b_view, a_view = mixed[:, :, :G], mixed[:, :, G:]
+    p_packed = torch.from_numpy(pool_np).to(dev)
+    out = torch.empty_like(o_dense)
+    gdn.gdn_gating_delta_rule_update(d["q"], d["k"], d["v"], a_view, b_view, d["A_log"],
+                                     d["dt_bias"], p_packed, d["state_idx"], None, out,
+                                     tokens_per_seq=wl.tokens_per_seq, state_layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_dense) and torch.equal(p_packed, p_dense)
+    g1, b1 = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], num_k_heads=Hk)
+    g2, b2 = gdn.gdn_gating(a_view, b_view, d["A_log"], d["dt_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(g1, g2) and torch.equal(b1, b2)
