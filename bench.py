@@ -172,6 +172,8 @@ def main():
                     help="0 auto, 1 column tiles, 2 row split, 3 value rows (VK layout)")
     ap.add_argument("--layout", default="KV", choices=["KV", "VK"],
                     help="storage order of the state tiles")
+    ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"],
+                    help="storage type of the state pool (the update runs in fp32 either way)")
     ap.add_argument("--block-v", type=int, default=0)
     ap.add_argument("--block-k", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
@@ -248,16 +250,20 @@ def main():
     pool = W.make_pool_torch(wl, dev)
     if args.layout == "VK":
         pool = pool.transpose(-1, -2).contiguous()
+    if args.state_dtype == "bf16":
+        pool = pool.to(torch.bfloat16)
     act = torch.bfloat16 if wl.act == W.ACT_BF16 else torch.float32
     out = torch.empty(inp.num_tokens, wl.num_v_heads, wl.head_v_dim, dtype=act, device=dev)
     inter = None
     if wl.intermediates:
         inter = torch.empty((inp.num_tokens, wl.num_v_heads) + tuple(pool.shape[2:]),
-                            dtype=torch.float32, device=dev)
+                            dtype=pool.dtype, device=dev)
     # the oracle's copy of the first set's initial states, taken before any update
     pool_rows0 = None
     if args.cpu_budget > 0:
-        pool_rows0 = pool[idx_sets[0].clamp(min=0).long()].cpu().numpy()
+        rows0 = pool[idx_sets[0].clamp(min=0).long()]
+        pool_rows0 = (rows0.view(torch.int16).cpu().numpy().view(np.uint16)
+                      if args.state_dtype == "bf16" else rows0.cpu().numpy())
         if args.layout == "VK":
             pool_rows0 = np.ascontiguousarray(np.swapaxes(pool_rows0, -1, -2))
 
@@ -298,7 +304,7 @@ def main():
 
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     updates = W.active_updates(inp)
-    alg_bytes = W.algorithmic_bytes(inp)
+    alg_bytes = W.algorithmic_bytes(inp, state_bytes=2 if args.state_dtype == "bf16" else 4)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     value = updates * args.steps / wall
     info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
@@ -324,7 +330,7 @@ def main():
         "config": {"workload": wl.name, "num_seqs": B, "tokens": inp.num_tokens,
                    "num_k_heads": wl.num_k_heads, "num_v_heads": wl.num_v_heads,
                    "head_k_dim": wl.head_k_dim, "head_v_dim": wl.head_v_dim,
-                   "activations": wl.act, "state": "f32", "state_layout": args.layout,
+                   "activations": wl.act, "state": args.state_dtype, "state_layout": args.layout,
                    "pool_slots": wl.num_slots,
                    "slot_sets": sets, "kernel": KERNEL_NAMES[info.kernel_family],
                    "block_v": info.block_v, "block_k": info.block_k,

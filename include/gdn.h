@@ -112,6 +112,11 @@ typedef struct gdn_config {
                                 to (H_k, 2*H_v/H_k))                              */
     uint32_t flags;          /* GDN_FLAG_*                                       */
     int32_t state_layout;    /* GDN_LAYOUT_KV (0) or GDN_LAYOUT_VK (1)           */
+    int32_t state_dtype;     /* storage of state_pool and intermediate_states:
+                                GDN_DTYPE_F32 (0, default) or GDN_DTYPE_BF16.
+                                The update runs in fp32 either way; bf16 tiles
+                                are widened on load and rounded to nearest even
+                                on store (half the state traffic)              */
     /* Tiling overrides (0 = the library's static table).  They change the
      * order of the fp32 reductions, never the operation. */
     int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): with GDN_LAYOUT_KV, row split
@@ -161,8 +166,8 @@ void gdn_default_config(gdn_config* cfg);
  *  v        [N, H_v, V]   act_dtype; token stride v_stride_tok
  *  a, b     [N, H_v]      act_dtype (dense, or strided per ab_stride_*)
  *  A_log, dt_bias [H_v]   fp32
- *  state_pool [num_slots, H_v, K, V] fp32 (GDN_LAYOUT_KV) or
- *             [num_slots, H_v, V, K] (GDN_LAYOUT_VK); updated in place
+ *  state_pool [num_slots, H_v, K, V] (GDN_LAYOUT_KV) or [num_slots, H_v,
+ *             V, K] (GDN_LAYOUT_VK), fp32 or bf16 (state_dtype); updated in place
  *  state_idx  [B] int32: pool slot of sequence i; any negative value marks a
  *             padded sequence, which is skipped entirely (its pool rows, out
  *             rows and intermediate rows are neither read nor written)
@@ -173,8 +178,9 @@ void gdn_default_config(gdn_config* cfg);
  *             NULL: row t receives S after
  *             token t (so the last token's row equals the final state)
  *
- * Alignment: q, k, v, out, state_pool and intermediate_states 16-byte
- * aligned; q/k/v token strides multiples of 8 elements.
+ * Alignment: q, k, v and out 16-byte aligned; state_pool and
+ * intermediate_states 16-byte (fp32) or 8-byte (bf16) aligned; q/k/v token
+ * strides multiples of 8 elements.
  * Caller contract (undefined if broken; checked under GDN_FLAG_DEBUG_CHECKS):
  * non-negative slot indices are distinct and < num_slots; cu_seqlens is
  * non-decreasing from 0 to N.  Rows of out/intermediate_states that belong to
@@ -182,9 +188,9 @@ void gdn_default_config(gdn_config* cfg);
  */
 gdn_status gdn_gating_delta_rule_update(
     const void* q, const void* k, const void* v, const void* a, const void* b,
-    const float* A_log, const float* dt_bias, float* state_pool,
+    const float* A_log, const float* dt_bias, void* state_pool,
     const int32_t* state_idx, const int32_t* cu_seqlens, void* out,
-    float* intermediate_states, const gdn_config* cfg, void* stream);
+    void* intermediate_states, const gdn_config* cfg, void* stream);
 
 /*
  * The unfused pair, for callers that keep the gates as tensors (vLLM PR
@@ -204,17 +210,17 @@ gdn_status gdn_gating(const void* a, const void* b, const float* A_log, const fl
                       float* g, float* beta, const gdn_config* cfg, void* stream);
 
 gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, float* state_pool, const int32_t* state_idx,
-                                const int32_t* cu_seqlens, void* out, float* intermediate_states,
+                                const float* beta, void* state_pool, const int32_t* state_idx,
+                                const int32_t* cu_seqlens, void* out, void* intermediate_states,
                                 const gdn_config* cfg, void* stream);
 
 /* Host-side argument check of gdn_gating_delta_rule_update (same arguments,
  * no stream); launches nothing and never touches device memory. */
 gdn_status gdn_validate(
     const void* q, const void* k, const void* v, const void* a, const void* b,
-    const float* A_log, const float* dt_bias, const float* state_pool,
+    const float* A_log, const float* dt_bias, const void* state_pool,
     const int32_t* state_idx, const int32_t* cu_seqlens, const void* out,
-    const float* intermediate_states, const gdn_config* cfg);
+    const void* intermediate_states, const gdn_config* cfg);
 
 /* The launch a valid configuration maps to (no device access). */
 gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens,

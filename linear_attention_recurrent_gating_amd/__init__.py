@@ -51,6 +51,7 @@ class GdnConfig(ctypes.Structure):
                 ("k_stride_tok", ctypes.c_int64), ("v_stride_tok", ctypes.c_int64),
                 ("ab_stride_tok", ctypes.c_int64), ("ab_stride_khead", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("state_layout", ctypes.c_int32),
+                ("state_dtype", ctypes.c_int32),
                 ("kernel_family", ctypes.c_int32),
                 ("block_v", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("waves_per_group", ctypes.c_int32)]
@@ -175,10 +176,10 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
                               or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous float32 [{Hv}] tensor")
     tile = (K, V) if _LAYOUTS[state_layout] == GDN_LAYOUT_KV else (V, K)
-    if (state_pool.dtype != torch.float32 or state_pool.dim() != 4
+    if (state_pool.dtype not in (torch.float32, torch.bfloat16) or state_pool.dim() != 4
             or tuple(state_pool.shape[1:]) != (Hv,) + tile or not state_pool.is_contiguous()):
-        raise ValueError(f"state_pool must be a contiguous float32 [slots, {Hv}, {tile[0]}, "
-                         f"{tile[1]}] tensor")
+        raise ValueError(f"state_pool must be a contiguous float32 or bfloat16 [slots, {Hv}, "
+                         f"{tile[0]}, {tile[1]}] tensor")
     if state_idx.dtype != torch.int32 or state_idx.dim() != 1 or not state_idx.is_contiguous():
         raise ValueError("state_idx must be a contiguous int32 [B] tensor")
     B = state_idx.shape[0]
@@ -187,11 +188,11 @@ def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seql
                                    or not cu_seqlens.is_contiguous()):
         raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor")
     if intermediate_states is not None and (
-            intermediate_states.dtype != torch.float32
+            intermediate_states.dtype != state_pool.dtype
             or tuple(intermediate_states.shape) != (N, Hv) + tile
             or not intermediate_states.is_contiguous()):
-        raise ValueError("intermediate_states must be a contiguous float32 tensor shaped like "
-                         "[N] + one pool row")
+        raise ValueError("intermediate_states must be a contiguous tensor of the pool's dtype "
+                         "shaped like [N] + one pool row")
     dev = q.device
     for t in (k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
               intermediate_states):
@@ -219,6 +220,7 @@ def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=
     cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim = Hk, Hv, K, V
     cfg.num_slots = state_pool.shape[0]
     cfg.state_layout = _LAYOUTS[state_layout]
+    cfg.state_dtype = GDN_DTYPE_BF16 if state_pool.dtype == torch.bfloat16 else GDN_DTYPE_F32
     if q.dtype == torch.bfloat16:
         cfg.act_dtype = GDN_DTYPE_BF16
     elif q.dtype == torch.float32:

@@ -189,6 +189,8 @@ gdn_status check_config(const gdn_config* cfg, bool has_cu) {
                     c.head_k_dim, c.head_v_dim);
     if (c.act_dtype != GDN_DTYPE_F32 && c.act_dtype != GDN_DTYPE_BF16)
         return fail(GDN_ERR_UNSUPPORTED_DTYPE, "act_dtype %d is neither F32 nor BF16", c.act_dtype);
+    if (c.state_dtype != GDN_DTYPE_F32 && c.state_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_UNSUPPORTED_DTYPE, "state_dtype %d is neither F32 nor BF16", c.state_dtype);
     if (c.num_tokens < 0) return fail(GDN_ERR_BAD_SHAPE, "num_tokens < 0");
     if (c.num_tokens > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "num_tokens exceeds 2^31-1");
     if (!has_cu) {
@@ -276,9 +278,9 @@ gdn_status check_ab_strides(const gdn_config& c) {
 // (g, beta).
 gdn_status validate_update(const void* q, const void* k, const void* v, const void* a, const void* b,
                            const float* A_log, const float* dt_bias, const float* g,
-                           const float* beta, const float* state_pool, const int32_t* state_idx,
+                           const float* beta, const void* state_pool, const int32_t* state_idx,
                            const int32_t* cu_seqlens, const void* out,
-                           const float* intermediate_states, const gdn_config* cfg) {
+                           const void* intermediate_states, const gdn_config* cfg) {
     g_last_error[0] = '\0';
     gdn_status s = check_config(cfg, cu_seqlens != nullptr);
     if (s != GDN_OK) return s;
@@ -286,6 +288,7 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
     if (s != GDN_OK) return s;
     if (cfg->num_seqs == 0) return GDN_OK;
     const size_t esize = cfg->act_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    const size_t state_align = cfg->state_dtype == GDN_DTYPE_BF16 ? 8 : 16;
     const bool pregated = g != nullptr;
     struct { const void* p; const char* name; size_t align; } ptrs[] = {
         {q, "q", 16}, {k, "k", 16}, {v, "v", 16},
@@ -293,7 +296,7 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
         {pregated ? beta : b, pregated ? "beta" : "b", pregated ? 4 : esize},
         {pregated ? g : A_log, pregated ? "g" : "A_log", 4},
         {pregated ? beta : dt_bias, pregated ? "beta" : "dt_bias", 4},
-        {state_pool, "state_pool", 16}, {state_idx, "state_idx", 4}, {out, "out", 16}};
+        {state_pool, "state_pool", state_align}, {state_idx, "state_idx", 4}, {out, "out", 16}};
     for (const auto& e : ptrs) {
         if (!e.p) return fail(GDN_ERR_NULL_POINTER, "%s is NULL", e.name);
         if (!aligned(e.p, e.align))
@@ -301,15 +304,15 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
     }
     if (cu_seqlens && !aligned(cu_seqlens, 4))
         return fail(GDN_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
-    if (intermediate_states && !aligned(intermediate_states, 16))
-        return fail(GDN_ERR_MISALIGNED, "intermediate_states is not 16-byte aligned");
+    if (intermediate_states && !aligned(intermediate_states, state_align))
+        return fail(GDN_ERR_MISALIGNED, "intermediate_states is not %zu-byte aligned", state_align);
     return GDN_OK;
 }
 
 gdn_status run_update(const void* q, const void* k, const void* v, const void* a, const void* b,
                       const float* A_log, const float* dt_bias, const float* g, const float* beta,
-                      float* state_pool, const int32_t* state_idx, const int32_t* cu_seqlens,
-                      void* out, float* intermediate_states, const gdn_config* cfg, void* stream) {
+                      void* state_pool, const int32_t* state_idx, const int32_t* cu_seqlens,
+                      void* out, void* intermediate_states, const gdn_config* cfg, void* stream) {
     gdn_status s = validate_update(q, k, v, a, b, A_log, dt_bias, g, beta, state_pool, state_idx,
                                    cu_seqlens, out, intermediate_states, cfg);
     if (s != GDN_OK) return s;
@@ -357,6 +360,7 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
     p.scale = c.scale > 0.0f ? c.scale : 1.0f / std::sqrt(static_cast<float>(c.head_k_dim));
     p.eps = c.l2norm_eps;
     p.write_final = (c.flags & GDN_FLAG_NO_FINAL_WRITEBACK) ? 0 : 1;
+    p.state_bf16 = c.state_dtype == GDN_DTYPE_BF16 ? 1 : 0;
 
     static const bool log = [] {
         const char* e = std::getenv("GDN_LOG");
@@ -364,12 +368,13 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
     }();
     if (log)
         std::fprintf(stderr,
-                     "[gdn] %s K=%d V=%d act=%s gates=%s multi_token=%d block_v=%d block_k=%d "
+                     "[gdn] %s K=%d V=%d act=%s state=%s gates=%s multi_token=%d block_v=%d block_k=%d "
                      "waves=%d chunk=%d groups=%lld lds=%d\n",
                      sh.kind == gdn::kKindRows        ? "rows"
                      : sh.kind == gdn::kKindValueRows ? "value-rows"
                                                       : "columns",
-                     sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", g ? "precomputed" : "fused",
+                     sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", p.state_bf16 ? "bf16" : "f32",
+                     g ? "precomputed" : "fused",
                      sh.multi_token, sh.block_v, sh.block_k, sh.waves, sh.chunk,
                      static_cast<long long>(sh.groups), sh.lds_bytes);
 
@@ -393,9 +398,9 @@ void gdn_default_config(gdn_config* cfg) {
 }
 
 gdn_status gdn_validate(const void* q, const void* k, const void* v, const void* a, const void* b,
-                        const float* A_log, const float* dt_bias, const float* state_pool,
+                        const float* A_log, const float* dt_bias, const void* state_pool,
                         const int32_t* state_idx, const int32_t* cu_seqlens, const void* out,
-                        const float* intermediate_states, const gdn_config* cfg) {
+                        const void* intermediate_states, const gdn_config* cfg) {
     return validate_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
                            cu_seqlens, out, intermediate_states, cfg);
 }
@@ -424,17 +429,17 @@ gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* 
 
 gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void* v, const void* a,
                                         const void* b, const float* A_log, const float* dt_bias,
-                                        float* state_pool, const int32_t* state_idx,
+                                        void* state_pool, const int32_t* state_idx,
                                         const int32_t* cu_seqlens, void* out,
-                                        float* intermediate_states, const gdn_config* cfg,
+                                        void* intermediate_states, const gdn_config* cfg,
                                         void* stream) {
     return run_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
                       cu_seqlens, out, intermediate_states, cfg, stream);
 }
 
 gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,
-                                const float* beta, float* state_pool, const int32_t* state_idx,
-                                const int32_t* cu_seqlens, void* out, float* intermediate_states,
+                                const float* beta, void* state_pool, const int32_t* state_idx,
+                                const int32_t* cu_seqlens, void* out, void* intermediate_states,
                                 const gdn_config* cfg, void* stream) {
     g_last_error[0] = '\0';
     if (!g || !beta) {
@@ -450,6 +455,8 @@ gdn_status gdn_gating(const void* a, const void* b, const float* A_log, const fl
     g_last_error[0] = '\0';
     if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
     const gdn_config& c = *cfg;
+    if (c.state_dtype != GDN_DTYPE_F32 && c.state_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_UNSUPPORTED_DTYPE, "state_dtype %d is neither F32 nor BF16", c.state_dtype);
     if (c.num_tokens < 0) return fail(GDN_ERR_BAD_SHAPE, "num_tokens < 0");
     if (c.num_k_heads < 1 || c.num_v_heads < 1 || c.num_v_heads % c.num_k_heads != 0)
         return fail(GDN_ERR_BAD_SHAPE, "H_v = %d must be a positive multiple of H_k = %d",

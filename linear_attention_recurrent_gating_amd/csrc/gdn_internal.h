@@ -19,11 +19,11 @@ struct FusedParams {
     const float* beta;          // precomputed beta [N, H_v] (with g)
     const float* A_log;
     const float* dt_bias;
-    float* pool;
+    void* pool;                 // state tiles, fp32 or bf16 (state_bf16)
     const int32_t* state_idx;
     const int32_t* cu_seqlens;  // nullptr: T tokens per sequence
     void* out;
-    float* inter;               // nullptr: no intermediate states
+    void* inter;                // nullptr: no intermediate states (same storage type)
     int64_t q_stride;           // elements between tokens
     int64_t k_stride;
     int64_t v_stride;
@@ -38,6 +38,7 @@ struct FusedParams {
     float scale;
     float eps;
     int32_t write_final;        // 0 under GDN_FLAG_NO_FINAL_WRITEBACK
+    int32_t state_bf16;         // 1: pool and intermediates hold bf16
 };
 
 // Kernel families.

@@ -46,29 +46,66 @@ constexpr int kMaxThreads = 512;
 // sits in SGPRs, each lane keeps one 32-bit byte offset in a VGPR, and the
 // row-group step is a scalar offset -- no 64-bit address per row stays live
 // between the loads and the final stores.  Offsets past the tile would be
-// clamped by the hardware (loads return 0, stores are dropped).
+// clamped by the hardware (loads return 0, stores are dropped).  Tiles may be
+// stored as bf16 (64-bit accesses per four elements, rounded to nearest even
+// on the way out); the state is fp32 in registers either way.
 constexpr int kBufNonTemporal = 2;           // cache-policy bit "nt" (gfx94x/gfx950)
 // Word 3 of a gfx9-family raw buffer resource: 32-bit data format, no swizzle.
 constexpr int kBufWord3 = 0x00020000;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, static_cast<int>(bytes),
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
                                              kBufWord3);
 }
 
-__device__ __forceinline__ float4 load_state(__amdgpu_buffer_rsrc_t r, uint32_t lane_bytes,
-                                             uint32_t row_bytes) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, lane_bytes, row_bytes, kBufNonTemporal);
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One K x V state tile in the pool or in intermediate_states, stored as fp32
+// or as bf16 (the arithmetic is fp32 either way).  Offsets are in elements;
+// `lane` is this lane's element offset within the tile.
+struct TileIO {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t lane_bytes;
+    bool bf16;
+};
+
+__device__ __forceinline__ TileIO tile_io(const void* base, bool bf16, size_t tile_index,
+                                          size_t tile_elems, uint32_t lane) {
+    const int sh = bf16 ? 1 : 2;
+    const char* b = static_cast<const char*>(base) + ((tile_index * tile_elems) << sh);
+    TileIO t;
+    t.r = tile_rsrc(b, static_cast<uint32_t>(tile_elems << sh));
+    t.lane_bytes = lane << sh;
+    t.bf16 = bf16;
+    return t;
+}
+
+// Four consecutive state elements at element offset `off` past the lane's.
+__device__ __forceinline__ float4 tile_load(const TileIO& t, uint32_t off) {
+    if (t.bf16) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(t.r, t.lane_bytes, off << 1,
+                                                             kBufNonTemporal);
+        return make_float4(__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                           __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u));
+    }
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(t.r, t.lane_bytes, off << 2, kBufNonTemporal);
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                        __uint_as_float(v[3]));
 }
 
-__device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, uint32_t lane_bytes,
-                                            uint32_t row_bytes, const float4& s) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f);
+
+__device__ __forceinline__ void tile_store(const TileIO& t, uint32_t off, const float4& s) {
+    if (t.bf16) {
+        const u32x2 v = {bf16_rne_bits(s.x) | (bf16_rne_bits(s.y) << 16),
+                         bf16_rne_bits(s.z) | (bf16_rne_bits(s.w) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, t.r, t.lane_bytes, off << 1, kBufNonTemporal);
+        return;
+    }
     const u32x4 v = {__float_as_uint(s.x), __float_as_uint(s.y), __float_as_uint(s.z),
                      __float_as_uint(s.w)};
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, lane_bytes, row_bytes, kBufNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(v, t.r, t.lane_bytes, off << 2, kBufNonTemporal);
 }
 
 // ---------------------------------------------------------------- conversions
@@ -81,6 +118,8 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return bf16_rne(f); }
 
 // N consecutive activation elements starting at element `e`, widened to fp32.
 // ACT 0 = fp32, 1 = bf16.  The start is aligned to min(16, N*size) bytes.
@@ -343,18 +382,16 @@ gdn_fused_update(const FusedParams p) {
     const int rg = lane / LPR;
 
     const size_t tile_elems = static_cast<size_t>(K) * p.V;
-    const uint32_t tile_bytes = static_cast<uint32_t>(tile_elems * sizeof(float));
-    const __amdgpu_buffer_rsrc_t tile_r =
-        tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * tile_elems, tile_bytes);
     // element (rg + RG*i, col) of a tile: lane offset + i row-group steps
-    const uint32_t row_step = static_cast<uint32_t>(RG * p.V * sizeof(float));
-    const uint32_t lane_bytes = static_cast<uint32_t>((rg * p.V + col) * sizeof(float));
+    const uint32_t row_step = static_cast<uint32_t>(RG * p.V);
+    const uint32_t lane_elem = static_cast<uint32_t>(rg * p.V + col);
+    const TileIO tio = tile_io(p.pool, p.state_bf16, static_cast<size_t>(slot) * p.Hv + h,
+                               tile_elems, lane_elem);
 
     // State tile -> VGPRs.  Issued first so the loads overlap the set-up below.
     float4 S[RPL];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i)
-        S[i] = load_state(tile_r, lane_bytes, i * row_step);
+    for (int i = 0; i < RPL; ++i) S[i] = tile_load(tio, i * row_step);
 
 
     for (int64_t c0 = t0; c0 < t1; c0 += CHUNK) {
@@ -452,11 +489,10 @@ gdn_fused_update(const FusedParams p) {
                 S[i].w = __builtin_fmaf(kh[i], u.w, gamma * S[i].w);
             }
             if (p.inter) {
-                const __amdgpu_buffer_rsrc_t it_r =
-                    tile_rsrc(p.inter + (static_cast<size_t>(t) * p.Hv + h) * tile_elems, tile_bytes);
+                const TileIO it = tile_io(p.inter, p.state_bf16, static_cast<size_t>(t) * p.Hv + h,
+                                          tile_elems, lane_elem);
 #pragma unroll
-                for (int i = 0; i < RPL; ++i)
-                    store_state(it_r, lane_bytes, i * row_step, S[i]);
+                for (int i = 0; i < RPL; ++i) tile_store(it, i * row_step, S[i]);
             }
         }
         if (c0 + CHUNK < t1) lds_barrier();   // the next chunk reuses the LDS
@@ -464,8 +500,7 @@ gdn_fused_update(const FusedParams p) {
 
     if (p.write_final) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-            store_state(tile_r, lane_bytes, i * row_step, S[i]);
+        for (int i = 0; i < RPL; ++i) tile_store(tio, i * row_step, S[i]);
     }
 }
 
@@ -571,15 +606,13 @@ gdn_decode_rows(const FusedParams p) {
     float vv[4];
     load_act<ACT, 4>(p.v, t * p.v_stride + static_cast<int64_t>(h) * V + col, vv);
 
-    constexpr uint32_t tile_bytes = static_cast<uint32_t>(K * V * sizeof(float));
-    const __amdgpu_buffer_rsrc_t tile_r =
-        tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * (K * V), tile_bytes);
-    constexpr uint32_t row_step = RG * V * sizeof(float);   // one kilobyte
-    const uint32_t lane_bytes = static_cast<uint32_t>(((kw * RPW + rg) * V + col) * sizeof(float));
+    constexpr uint32_t row_step = RG * V;   // one kilobyte of fp32 state
+    const uint32_t lane_elem = static_cast<uint32_t>((kw * RPW + rg) * V + col);
+    const TileIO tio = tile_io(p.pool, p.state_bf16, static_cast<size_t>(slot) * p.Hv + h, K * V, lane_elem);
 
     float4 S[RPL];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) S[i] = load_state(tile_r, lane_bytes, i * row_step);
+    for (int i = 0; i < RPL; ++i) S[i] = tile_load(tio, i * row_step);
 
     // rows kw*RPW + RG*i + rg of the head sit at kw*RPW + rg*RPL + i
     qk.finish(p, qs, ks, lane, [](int kappa) {
@@ -648,14 +681,13 @@ gdn_decode_rows(const FusedParams p) {
         S[i].w = __builtin_fmaf(kh[i], u.w, gamma * S[i].w);
     }
     if (p.inter) {
-        const __amdgpu_buffer_rsrc_t it_r =
-            tile_rsrc(p.inter + (static_cast<size_t>(t) * p.Hv + h) * (K * V), tile_bytes);
+        const TileIO it = tile_io(p.inter, p.state_bf16, static_cast<size_t>(t) * p.Hv + h, K * V, lane_elem);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) store_state(it_r, lane_bytes, i * row_step, S[i]);
+        for (int i = 0; i < RPL; ++i) tile_store(it, i * row_step, S[i]);
     }
     if (p.write_final) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) store_state(tile_r, lane_bytes, i * row_step, S[i]);
+        for (int i = 0; i < RPL; ++i) tile_store(tio, i * row_step, S[i]);
     }
 }
 
@@ -679,8 +711,8 @@ struct ValueRows {
     static constexpr int RPL = (V / RG < 8) ? V / RG : 8;           // rows per lane
     static constexpr int RPW = RPL * RG;                            // rows per wave
     static constexpr int VW = V / RPW;                              // waves per head
-    static constexpr uint32_t ROW_STEP = RG * K * sizeof(float);    // bytes between a lane's rows
-    static constexpr uint32_t HALF = LPR * 4 * sizeof(float);       // bytes between a lane's chunks
+    static constexpr uint32_t ROW_STEP = RG * K;                    // elements between a lane's rows
+    static constexpr uint32_t HALF = LPR * 4;                       // elements between a lane's chunks
 };
 
 // Loads this lane's keys of one q or k vector: chunks at 4c and 4(c+LPR).
@@ -796,16 +828,13 @@ gdn_vk_decode(const FusedParams p) {
 #pragma unroll
     for (int i = 0; i < RPL; ++i) vv[i] = load_scalar<ACT>(p.v, vbase + RG * i);
 
-    constexpr uint32_t tile_bytes = static_cast<uint32_t>(K * V * sizeof(float));
-    const __amdgpu_buffer_rsrc_t tile_r =
-        tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * (K * V), tile_bytes);
-    const uint32_t lane_bytes = static_cast<uint32_t>((row0 * K + 4 * c) * sizeof(float));
+    const uint32_t lane_elem = static_cast<uint32_t>(row0 * K + 4 * c);
+    const TileIO tio = tile_io(p.pool, p.state_bf16, static_cast<size_t>(slot) * p.Hv + h, K * V, lane_elem);
     float4 S[RPL][2];
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            S[i][hh] = load_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF);
+        for (int hh = 0; hh < 2; ++hh) S[i][hh] = tile_load(tio, i * L::ROW_STEP + hh * L::HALF);
 
     float qh[8], kh[8], kq;
     normalize_keys<LPR>(qx, kx, p.scale, p.eps, qh, kh, kq);
@@ -817,20 +846,17 @@ gdn_vk_decode(const FusedParams p) {
         if (c == 0) store1_act<ACT>(p.out, obase + RG * i, o);
     }
     if (p.inter) {
-        const __amdgpu_buffer_rsrc_t it_r =
-            tile_rsrc(p.inter + (static_cast<size_t>(t) * p.Hv + h) * (K * V), tile_bytes);
+        const TileIO it = tile_io(p.inter, p.state_bf16, static_cast<size_t>(t) * p.Hv + h, K * V, lane_elem);
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                store_state(it_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+            for (int hh = 0; hh < 2; ++hh) tile_store(it, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
     }
     if (p.write_final) {
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                store_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+            for (int hh = 0; hh < 2; ++hh) tile_store(tio, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
     }
 }
 
@@ -886,16 +912,13 @@ gdn_vk_multi(const FusedParams p) {
     const int row0 = pl.vw * RPW + rg;
     float* vs = lds + 2 * CHUNK * K + wave * (CHUNK * RPW);   // [CHUNK][RPW] this wave's v
 
-    constexpr uint32_t tile_bytes = static_cast<uint32_t>(K * V * sizeof(float));
-    const __amdgpu_buffer_rsrc_t tile_r =
-        tile_rsrc(p.pool + (static_cast<size_t>(slot) * p.Hv + h) * (K * V), tile_bytes);
-    const uint32_t lane_bytes = static_cast<uint32_t>((row0 * K + 4 * c) * sizeof(float));
+    const uint32_t lane_elem = static_cast<uint32_t>(row0 * K + 4 * c);
+    const TileIO tio = tile_io(p.pool, p.state_bf16, static_cast<size_t>(slot) * p.Hv + h, K * V, lane_elem);
     float4 S[RPL][2];
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            S[i][hh] = load_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF);
+        for (int hh = 0; hh < 2; ++hh) S[i][hh] = tile_load(tio, i * L::ROW_STEP + hh * L::HALF);
 
 
     for (int64_t c0 = t0; c0 < t1; c0 += CHUNK) {
@@ -932,13 +955,12 @@ gdn_vk_multi(const FusedParams p) {
                 if (c == 0) store1_act<ACT>(p.out, obase + RG * i, o);
             }
             if (p.inter) {
-                const __amdgpu_buffer_rsrc_t it_r =
-                    tile_rsrc(p.inter + (static_cast<size_t>(t) * p.Hv + h) * (K * V), tile_bytes);
+                const TileIO it =
+                    tile_io(p.inter, p.state_bf16, static_cast<size_t>(t) * p.Hv + h, K * V, lane_elem);
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        store_state(it_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+                    for (int hh = 0; hh < 2; ++hh) tile_store(it, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
             }
         }
         if (c0 + CHUNK < t1) lds_barrier();   // the next chunk reuses the LDS
@@ -948,8 +970,7 @@ gdn_vk_multi(const FusedParams p) {
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                store_state(tile_r, lane_bytes, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
+            for (int hh = 0; hh < 2; ++hh) tile_store(tio, i * L::ROW_STEP + hh * L::HALF, S[i][hh]);
     }
 }
 

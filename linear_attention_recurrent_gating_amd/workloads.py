@@ -195,14 +195,15 @@ def active_updates(inp: HostInputs) -> int:
     return int(inp.lengths[live].sum()) * inp.wl.num_v_heads
 
 
-def algorithmic_bytes(inp: HostInputs, final_writeback: bool = True) -> int:
+def algorithmic_bytes(inp: HostInputs, final_writeback: bool = True, state_bytes: int = 4) -> int:
     """Bytes the update must move: state read + (intermediates) + final write of
     every live (sequence, v-head), plus every token's activations and the
-    per-call parameters.  Re-reads of shared q/k are not counted."""
+    per-call parameters.  Re-reads of shared q/k are not counted.
+    state_bytes: 4 for an fp32 state pool, 2 for bf16 storage."""
     wl = inp.wl
     e = 2 if wl.act == ACT_BF16 else 4
     K, V, Hk, Hv = wl.head_k_dim, wl.head_v_dim, wl.num_k_heads, wl.num_v_heads
-    tile = K * V * 4
+    tile = K * V * state_bytes
     live = inp.state_idx >= 0
     nlive = int(live.sum())
     state = nlive * Hv * tile * (1 + (1 if final_writeback else 0))

@@ -46,7 +46,7 @@ def _load(path: str = _LIB):
                       ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                       ctypes.c_int64, ctypes.c_double, ctypes.c_double,
-                      ctypes.c_int, ctypes.c_int, ctypes.c_int]
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         f.restype = ctypes.c_int
         fg = lib.gdn_oracle_gating
         fg.argtypes = [P] * 6 + [ctypes.c_int64, ctypes.c_int]
@@ -64,7 +64,8 @@ def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
            intermediates: bool = False, no_final_writeback: bool = False,
            threads: int = 0, lib_path: str = _LIB, state_layout: str = "KV"):
     """Run the oracle.  ``pool`` (float32 [slots, H_v, K, V], or [slots, H_v,
-    V, K] with state_layout "VK") is updated in place.  Returns ``(out, inter)``: out is float64 [N, H_v, V] (rows of
+    V, K] with state_layout "VK"; uint16 bf16 bit patterns for bf16 state
+    storage) is updated in place.  Returns ``(out, inter)``: out is float64 [N, H_v, V] (rows of
     untouched tokens stay NaN), inter is float32 [N, H_v, K, V] (NaN where not
     written) or None.  ``lib_path`` selects another build of the same source."""
     lib = _load(lib_path)
@@ -78,8 +79,10 @@ def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
     dt_bias = np.ascontiguousarray(dt_bias, dtype=d)
     idx = np.ascontiguousarray(state_idx, dtype=np.int32)
     cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
-    if pool.dtype != np.float32 or not pool.flags.c_contiguous:
-        raise ValueError("pool must be a C-contiguous float32 array (updated in place)")
+    if pool.dtype not in (np.float32, np.uint16) or not pool.flags.c_contiguous:
+        raise ValueError("pool must be a C-contiguous float32 or uint16 (bf16) array "
+                         "(updated in place)")
+    bf16 = pool.dtype == np.uint16
     N, Hk, K = q.shape
     Hv, V = v.shape[1], v.shape[2]
     if k.shape != q.shape or v.shape[0] != N or a.shape != (N, Hv) or b.shape != (N, Hv):
@@ -90,14 +93,19 @@ def update(q, k, v, a, b, A_log, dt_bias, pool, state_idx, cu_seqlens=None,
     if pool.shape[1:] != (Hv,) + tile:
         raise ValueError(f"pool shape must be [slots, H_v, {tile[0]}, {tile[1]}]")
     out = np.full((N, Hv, V), np.nan, dtype=d)
-    inter = np.full((N, Hv) + tile, np.nan, dtype=np.float32) if intermediates else None
+    if not intermediates:
+        inter = None
+    elif bf16:
+        inter = np.full((N, Hv) + tile, 0x7fc0, dtype=np.uint16)   # bf16 NaN where not written
+    else:
+        inter = np.full((N, Hv) + tile, np.nan, dtype=np.float32)
     B = idx.shape[0]
     rc = lib.gdn_oracle_update(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
                                _ptr(A_log), _ptr(dt_bias), _ptr(pool), _ptr(idx),
                                _ptr(cu), _ptr(out), _ptr(inter),
                                B, tokens_per_seq, N, Hk, Hv, K, V, pool.shape[0],
                                float(scale), float(eps), int(no_final_writeback),
-                               0 if state_layout == "KV" else 1, int(threads))
+                               0 if state_layout == "KV" else 1, 1 if bf16 else 0, int(threads))
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out, inter

@@ -26,7 +26,9 @@
  * token.  The pool stores each K x V tile either with V fastest ("KV",
  * element (kappa, c) at kappa*V + c) or transposed with K fastest ("VK",
  * element (kappa, c) at c*K + kappa); intermediate states use the same
- * layout.  Readings where the pages are silent: eps sits inside the square
+ * layout.  Tiles are stored as fp32 or as bf16; a bf16 tile is widened
+ * exactly on load and each stored element is the double-precision state
+ * rounded straight to the nearest bf16 (ties to even).  Readings where the pages are silent: eps sits inside the square
  * root; a sequence with state_idx < 0 or with no tokens is not touched at all;
  * intermediate_states[t, h] holds S after token t at global token row t.
  *
@@ -47,9 +49,57 @@
 #define ORACLE_LAYOUT_KV 0
 #define ORACLE_LAYOUT_VK 1
 
+#define ORACLE_STATE_F32 0
+#define ORACLE_STATE_BF16 1
+
 #define ORACLE_OK 0
 #define ORACLE_ERR_ARG 1
 #define ORACLE_ERR_NOMEM 2
+
+/* The bit pattern of the bf16 nearest to x (8 significant bits, ties to
+ * even), rounded once from double. */
+static uint16_t oracle_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    double y = x;
+    const double ax = fabs(x);
+    if (ax != 0.0 && !isinf(x)) {
+        if (ax < 0x1p-126) {                /* subnormal range: quantum 2^-133 */
+            y = nearbyint(x * 0x1p133) * 0x1p-133;
+        } else {
+            int e;
+            const double m = frexp(x, &e);  /* x = m 2^e, 0.5 <= |m| < 1 */
+            y = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+        }
+    }
+    const float f = (float)y;               /* exact (or inf on overflow) */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+static double oracle_from_bf16(uint16_t bits)
+{
+    const uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Element e of a state tile stored as fp32 or bf16. */
+static double tile_get(const void *tile, size_t e, int bf16)
+{
+    return bf16 ? oracle_from_bf16(((const uint16_t *)tile)[e]) : (double)((const float *)tile)[e];
+}
+
+static void tile_put(void *tile, size_t e, double x, int bf16)
+{
+    if (bf16)
+        ((uint16_t *)tile)[e] = oracle_to_bf16(x);
+    else
+        ((float *)tile)[e] = (float)x;
+}
 
 /* log(1 + e^x) without overflow. */
 static double oracle_softplus(double x)
@@ -89,22 +139,29 @@ static void oracle_l2norm(const double *x, double *y, int n, double eps, double 
  * no_final_writeback != 0 leaves the pool unchanged
  * state_layout: ORACLE_LAYOUT_KV or ORACLE_LAYOUT_VK (storage order of the
  *   pool and intermediate tiles)
+ * state_dtype: ORACLE_STATE_F32 or ORACLE_STATE_BF16 (pool and intermediates
+ *   hold float or bf16 bit patterns)
  * scale <= 0 selects K^-1/2.  threads <= 0 uses the OpenMP default.
  */
 int gdn_oracle_update(const double *q, const double *k, const double *v,
                       const double *a, const double *b,
                       const double *A_log, const double *dt_bias,
-                      float *pool, const int32_t *state_idx,
+                      void *pool, const int32_t *state_idx,
                       const int32_t *cu_seqlens, double *out,
-                      float *intermediate,
+                      void *intermediate,
                       int B, int T, int64_t N, int Hk, int Hv, int K, int V,
                       int64_t num_slots, double scale, double eps,
-                      int no_final_writeback, int state_layout, int threads)
+                      int no_final_writeback, int state_layout, int state_dtype,
+                      int threads)
 {
     if (B < 0 || K <= 0 || V <= 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0)
         return ORACLE_ERR_ARG;
     if (state_layout != ORACLE_LAYOUT_KV && state_layout != ORACLE_LAYOUT_VK)
         return ORACLE_ERR_ARG;
+    if (state_dtype != ORACLE_STATE_F32 && state_dtype != ORACLE_STATE_BF16)
+        return ORACLE_ERR_ARG;
+    const int bf16 = state_dtype == ORACLE_STATE_BF16;
+    const size_t esize = bf16 ? 2 : 4;
     /* storage strides of S[kappa][c] inside a tile */
     const size_t row_stride = state_layout == ORACLE_LAYOUT_KV ? (size_t)V : 1;
     const size_t col_stride = state_layout == ORACLE_LAYOUT_KV ? 1 : (size_t)K;
@@ -163,10 +220,10 @@ int gdn_oracle_update(const double *q, const double *k, const double *v,
             status = ORACLE_ERR_NOMEM;
             continue;
         }
-        float *tile = pool + ((size_t)slot * Hv + h) * (size_t)K * V;
+        char *tile = (char *)pool + ((size_t)slot * Hv + h) * (size_t)K * V * esize;
         for (int kk = 0; kk < K; ++kk)
             for (int c = 0; c < V; ++c)
-                S[(size_t)kk * V + c] = (double)tile[kk * row_stride + c * col_stride];
+                S[(size_t)kk * V + c] = tile_get(tile, kk * row_stride + c * col_stride, bf16);
 
         for (int64_t t = t0; t < t1; ++t) {
             /* gating: decay g and write strength beta */
@@ -201,16 +258,16 @@ int gdn_oracle_update(const double *q, const double *k, const double *v,
                 ot[c] = o;
             }
             if (intermediate) {
-                float *it = intermediate + ((size_t)t * Hv + h) * (size_t)K * V;
+                char *it = (char *)intermediate + ((size_t)t * Hv + h) * (size_t)K * V * esize;
                 for (int kk = 0; kk < K; ++kk)
                     for (int c = 0; c < V; ++c)
-                        it[kk * row_stride + c * col_stride] = (float)S[(size_t)kk * V + c];
+                        tile_put(it, kk * row_stride + c * col_stride, S[(size_t)kk * V + c], bf16);
             }
         }
         if (!no_final_writeback)
             for (int kk = 0; kk < K; ++kk)
                 for (int c = 0; c < V; ++c)
-                    tile[kk * row_stride + c * col_stride] = (float)S[(size_t)kk * V + c];
+                    tile_put(tile, kk * row_stride + c * col_stride, S[(size_t)kk * V + c], bf16);
         free(S); free(kh); free(qh); free(u);
     }
     return status;

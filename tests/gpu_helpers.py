@@ -81,7 +81,7 @@ def run_gpu(inp, pool, device, intermediates=None, flags=0, block_v=0, waves_per
     inter = None
     if intermediates:
         tile = (wl.head_k_dim, wl.head_v_dim) if layout == "KV" else (wl.head_v_dim, wl.head_k_dim)
-        inter = torch.full((N, wl.num_v_heads) + tile, float("nan"), dtype=torch.float32,
+        inter = torch.full((N, wl.num_v_heads) + tile, float("nan"), dtype=pool.dtype,
                            device=device)
     gdn.gdn_gating_delta_rule_update(
         d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool, d["state_idx"],
@@ -112,7 +112,8 @@ def oracle_on_seqs(inp, pool0_rows, seqs, intermediates=False, no_final_writebac
     [.., V, K] for layout "VK") holds their initial states.  Returns (out rows,
     final states, inter rows, rows) in that layout."""
     d, rows = sub_inputs(inp, seqs)
-    pool = np.ascontiguousarray(pool0_rows, dtype=np.float32).copy()
+    pool = np.ascontiguousarray(pool0_rows).copy()   # float32, or uint16 bf16 bit patterns
+    assert pool.dtype in (np.float32, np.uint16)
     out, inter = oracle.update(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
                                pool, d["state_idx"], d["cu_seqlens"], intermediates=intermediates,
                                no_final_writeback=no_final_writeback, state_layout=layout)

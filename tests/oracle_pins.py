@@ -426,8 +426,42 @@ def pin_gating_step(upd):
     assert abs(np.exp(g[0, 2]) - 0.5 ** np.exp(-0.7)) < 1e-15  # x = 0: (1+1)^(-A)
 
 
+def _bf16_bits(x):
+    """bf16 bit patterns of values that are exactly bf16 (no rounding here)."""
+    u = np.asarray(x, np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def _from_bf16(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+def pin_bf16_state_storage(upd):
+    """bf16 state storage on the worked example: the state stays in double
+    between tokens and every stored element is the exact value rounded once to
+    the nearest bf16 (8 significant bits), hand-derived:
+      S1 = [[.35, .04], [1.3, .72]]   -> [[179/512, 41/1024], [83/64, 23/32]]
+      S2 = [[.175, .02], [1.325, 1.18]] -> [[179/1024, 41/2048], [85/64, 151/128]]
+    (1.325*64 = 84.8 rounds up to 85; 0.175*1024 = 179.2 rounds down)."""
+    q = np.array([[[0.0, 5.0]], [[1.0, 0.0]]])
+    k = np.array([[[3.0, 4.0]], [[0.0, 2.0]]])
+    v = np.array([[[1.0, -1.0]], [[2.0, 2.0]]])
+    z = np.zeros((2, 1))
+    pool = _bf16_bits([[[[1.0, 2.0], [3.0, 4.0]]]])
+    out, inter = upd(q, k, v, z, z, np.zeros(1), np.zeros(1), pool, np.array([0], np.int32),
+                     None, tokens_per_seq=2, scale=1.0, eps=0.0, intermediates=True)
+    assert inter.dtype == np.uint16
+    s1 = np.array([[179 / 512, 41 / 1024], [83 / 64, 23 / 32]])
+    s2 = np.array([[179 / 1024, 41 / 2048], [85 / 64, 151 / 128]])
+    assert np.array_equal(_from_bf16(inter[0, 0]), s1.astype(np.float32)), "bf16 S1"
+    assert np.array_equal(_from_bf16(pool[0, 0]), s2.astype(np.float32)), "bf16 final state"
+    assert np.array_equal(inter[1], pool[0]), "last intermediate != final state (bf16)"
+    _close(out[1, 0], [0.175, 0.02], 1e-13, "bf16 storage leaves the outputs in double")
+
+
 ALL_PINS = [pin_worked_example, pin_gamma_closed_form, pin_beta_closed_form,
             pin_unit_write, pin_write_and_orthogonal_complement,
             pin_zero_state_output, pin_eps_inside_root, pin_matrix_form,
             pin_chain, pin_gqa_is_mha, pin_scale_invariance, pin_structure,
-            pin_state_layouts, pin_gating_step]
+            pin_state_layouts, pin_gating_step, pin_bf16_state_storage]

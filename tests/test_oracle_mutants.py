@@ -32,10 +32,12 @@ MUTANTS = {
                             "const double gamma = exp(0.5 * g);"),
     "sigmoid_sign": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
     "dt_bias_dropped": ("a[t * Hv + h] + dt_bias[h]", "a[t * Hv + h]"),
-    "no_writeback": ("                    tile[kk * row_stride + c * col_stride] = (float)S[(size_t)kk * V + c];",
-                     "                    tile[kk * row_stride + c * col_stride] = tile[kk * row_stride + c * col_stride];"),
-    "layout_ignored_on_load": ("S[(size_t)kk * V + c] = (double)tile[kk * row_stride + c * col_stride];",
-                               "S[(size_t)kk * V + c] = (double)tile[(size_t)kk * V + c];"),
+    "no_writeback": ("                    tile_put(tile, kk * row_stride + c * col_stride, S[(size_t)kk * V + c], bf16);",
+                     "                    (void)0;"),
+    "layout_ignored_on_load": ("S[(size_t)kk * V + c] = tile_get(tile, kk * row_stride + c * col_stride, bf16);",
+                               "S[(size_t)kk * V + c] = tile_get(tile, (size_t)kk * V + c, bf16);"),
+    "bf16_truncates": ("y = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "y = ldexp(trunc(ldexp(m, 8)), e - 8);"),
+    "bf16_one_bit_short": ("y = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "y = ldexp(nearbyint(ldexp(m, 7)), e - 7);"),
     "gating_head_index": ("g[e] = -exp(A_log[h]) * oracle_softplus(a[e] + dt_bias[h]);",
                           "g[e] = -exp(A_log[0]) * oracle_softplus(a[e] + dt_bias[h]);"),
     "gating_beta_from_a": ("beta[e] = oracle_sigmoid(b[e]);", "beta[e] = oracle_sigmoid(a[e]);"),

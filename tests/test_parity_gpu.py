@@ -565,3 +565,67 @@ def test_packed_mixed_ba(dev, layout):
     g2, b2 = gdn.gdn_gating(a_view, b_view, d["A_log"], d["dt_bias"])
     torch.cuda.synchronize()
     assert torch.equal(g1, g2) and torch.equal(b1, b2)
+
+
+# ------------------------------------------------------- bf16 state storage
+def _bf16_within_one_ulp(got_bits, ref_bits):
+    """True where two stored bf16 values differ by at most one bf16 ulp (of
+    the larger magnitude), or by no more than the fp32 arithmetic noise
+    (1e-5 of the largest reference magnitude) for elements near zero, where
+    a tiny value's ulp is smaller than that noise."""
+    g = _bits_to_f32(got_bits).astype(np.float64)
+    r = _bits_to_f32(ref_bits).astype(np.float64)
+    mag = np.maximum(np.abs(g), np.abs(r))
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-38))) - 7)
+    return np.abs(g - r) <= np.maximum(ulp, 1e-5 * float(np.max(np.abs(r))))
+
+
+def _bits_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+STATE_BF16_CASES = [
+    ("KV", W.Workload("bf16state_decode", 90, 9, 1, 4, 8, 128, 128, W.ACT_BF16, 12, 0.05,
+                      num_padded=2)),
+    ("KV", W.Workload("bf16state_spec", 91, 6, 1, 4, 8, 128, 128, W.ACT_BF16, 8, 0.05,
+                      varlen=True, len_range=(1, 20), num_padded=1, intermediates=True)),
+    ("KV", W.Workload("bf16state_cols_f32", 92, 5, 3, 2, 4, 64, 64, W.ACT_F32, 8, 0.05,
+                      intermediates=True)),
+    ("VK", W.Workload("bf16state_vk_decode", 93, 9, 1, 4, 8, 128, 128, W.ACT_BF16, 12, 0.05)),
+    ("VK", W.Workload("bf16state_vk_multi", 94, 4, 5, 2, 4, 64, 128, W.ACT_BF16, 6, 0.05,
+                      intermediates=True)),
+    ("KV", W.QWEN3NEXT_B64.with_(name="bf16state_qwen3next_b64", seed=95)),
+]
+
+
+@pytest.mark.parametrize("layout,wl", STATE_BF16_CASES,
+                         ids=lambda x: x if isinstance(x, str) else x.name)
+def test_bf16_state_storage(dev, layout, wl):
+    """State stored as bf16 (fp32 arithmetic): outputs to the activation
+    bar, stored states within one bf16 ulp of the oracle's single rounding,
+    untouched slots and padded rows bit-identical."""
+    import torch
+    announce(f"bf16 state {wl.name} {layout}")
+    inp = W.make_host_inputs(wl)
+    bits, _ = W.round_to_bf16(to_layout(W.make_pool_host(wl), layout))
+    pool = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    out, inter = run_gpu(inp, pool, dev, layout=layout)
+    seqs = np.arange(wl.num_seqs)
+    o_ref, s_ref, i_ref, _ = oracle_on_seqs(inp, bits[np.maximum(inp.state_idx, 0)], seqs,
+                                            intermediates=wl.intermediates, layout=layout)
+    live, dead = live_rows(inp)
+    out_np = to_np(out)
+    assert rel_err(out_np[live], o_ref[live]) <= tol_for(wl)
+    assert np.all(np.isnan(out_np[dead]))
+    after = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    lv = inp.state_idx >= 0
+    got = after[inp.state_idx[lv]]
+    assert np.all(_bf16_within_one_ulp(got, s_ref[lv])), "final state beyond one bf16 ulp"
+    assert rel_err(_bits_to_f32(got), _bits_to_f32(s_ref[lv])) <= 2e-2
+    assert np.mean(got == s_ref[lv]) > 0.99, "most stored elements should round identically"
+    untouched = np.setdiff1d(np.arange(wl.num_slots), inp.state_idx[lv])
+    assert np.array_equal(after[untouched], bits[untouched])
+    if wl.intermediates:
+        ib = inter.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.all(_bf16_within_one_ulp(ib[live], i_ref[live]))
+        assert np.all(ib[dead] == 0x7FC0), "padded rows of bf16 intermediates were written"
