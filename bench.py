@@ -30,16 +30,24 @@ from linear_attention_recurrent_gating_amd import workloads as W  # noqa: E402
 
 METRIC = "state updates/sec (seq·head·token) + HBM GB/s as % of peak, bs=512 decode"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc", "gdn_kernels.hip")
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+CSRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNEL_NAMES = {1: "gdn_fused_update", 2: "gdn_decode_rows", 3: "gdn_vk_update"}  # by kernel_family
+KERNEL_NAMES = {1: "gdn_fused_update", 2: "gdn_decode_rows", 3: "gdn_vk_update",
+                4: "gdn_chunk_fwd"}  # by kernel_family
+# The sources each kernel is compiled from (the counter profiles are keyed to them).
+KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_device.h", "gdn_internal.h")}
+DEFAULT_SOURCES = ("gdn_kernels.hip", "gdn_device.h", "gdn_internal.h")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str = "gdn_decode_rows") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(kernel, DEFAULT_SOURCES):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def profile_path(kernel: str, workload: str, kind: str) -> str:
@@ -58,7 +66,7 @@ def counter_traffic(kernel: str, workload: str):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     try:
         return int(float(vals["traffic_bytes_per_launch"]))
@@ -112,7 +120,7 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
     stats = _csv_rows(os.path.join(prof_dir, "trace", "run_kernel_stats.csv"))
     lines = [f"# rocprofv3 kernel-trace summary: {kernel}, workload {workload}",
              f"# command: {commands['trace']}",
-             f"# kernel source sha256[:16] = {kernel_source_hash()}",
+             f"# kernel source sha256[:16] = {kernel_source_hash(kernel)}",
              "# name | calls | average_us | min_us | max_us | percent"]
     import re
     for r in stats:
@@ -146,7 +154,7 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
            f"# command (WRITE_SIZE): {commands['write']}",
            f"# calibration: {commands['copy']} (1 GiB read + 1 GiB written per dispatch)",
            f"# summarised by: {commands['summary']}",
-           f"kernel_source_sha256_16 = {kernel_source_hash()}",
+           f"kernel_source_sha256_16 = {kernel_source_hash(kernel)}",
            f"fetch_kib_per_dispatch = {fetch:.1f}   # mean over {nf} dispatches",
            f"write_kib_per_dispatch = {write:.1f}   # mean over {nw} dispatches",
            f"copy_fetch_kib_per_dispatch = {cfetch:.1f}",
@@ -169,7 +177,8 @@ def main():
     ap.add_argument("--workload", default=W.DECODE_B512.name, choices=sorted(W.ALL))
     ap.add_argument("--slot-sets", type=int, default=8)
     ap.add_argument("--family", type=int, default=0,
-                    help="0 auto, 1 column tiles, 2 row split, 3 value rows (VK layout)")
+                    help="0 auto, 1 column tiles, 2 row split, 3 value rows (VK layout), "
+                         "4 chunked (64-token chunks on the matrix cores)")
     ap.add_argument("--layout", default="KV", choices=["KV", "VK"],
                     help="storage order of the state tiles")
     ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"],
@@ -192,7 +201,8 @@ def main():
 
     if args.summarize_profiles:
         d = args.summarize_profiles
-        run = f"python3 bench.py --workload {args.workload}"
+        run = f"python3 bench.py --workload {args.workload}" + (
+            f" --family {args.family}" if args.family else "")
         summarize_profiles(d, args.workload, args.kernel, {
             "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
                      f"{run} --steps 50 --warmup 5 --cpu-budget 0",
@@ -203,8 +213,7 @@ def main():
             "copy": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d "
                     f"{d}/copy_<counter> -o run -- python3 bench.py --copy-calibration --steps 3 "
                     f"--warmup 1",
-            "summary": f"python3 bench.py --workload {args.workload} --kernel {args.kernel} "
-                       f"--summarize-profiles {d}"})
+            "summary": f"{run} --kernel {args.kernel} --summarize-profiles {d}"})
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -306,6 +315,7 @@ def main():
     updates = W.active_updates(inp)
     alg_bytes = W.algorithmic_bytes(inp, state_bytes=2 if args.state_dtype == "bf16" else 4)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    chunked = args.family == gdn.GDN_KERNEL_CHUNKED
     value = updates * args.steps / wall
     info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
                                         tokens_per_seq=wl.tokens_per_seq,
@@ -347,6 +357,15 @@ def main():
                      "algorithmic_bytes": alg_bytes, "kernel": KERNEL_NAMES[info.kernel_family]},
         "cpu_baseline": None,
     }
+    if chunked:
+        # Dense products of the chunked form on the bf16 matrix cores.
+        flops = W.chunked_flops(inp)
+        tflops = flops / (kern_ms * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                           "traffic": counter_traffic(KERNEL_NAMES[4], wl.name),
+                           "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
+                           "kernel": KERNEL_NAMES[4]}
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(inp, pool_rows0, args.cpu_budget)
     print(json.dumps(res), flush=True)

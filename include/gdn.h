@@ -121,7 +121,8 @@ typedef struct gdn_config {
      * order of the fp32 reductions, never the operation. */
     int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): with GDN_LAYOUT_KV, row split
                                 for one token per sequence and column tiles
-                                otherwise; with GDN_LAYOUT_VK, value rows       */
+                                otherwise; with GDN_LAYOUT_VK, value rows.
+                                GDN_KERNEL_CHUNKED is never chosen by AUTO     */
     int32_t block_v;         /* column tiles: 8, 16, 32 or 64 V-columns per
                                 wavefront (dividing V).  A non-zero value with
                                 GDN_KERNEL_AUTO selects the column tiles        */
@@ -141,10 +142,15 @@ typedef struct gdn_config {
 #define GDN_KERNEL_VALUE_ROWS 3   /* GDN_LAYOUT_VK only: wavefront = (v-head,
                                      block of whole value-rows); any number of
                                      tokens                                    */
+#define GDN_KERNEL_CHUNKED 4      /* workgroup = (sequence, v-head): 64-token
+                                     chunks in the WY form on the matrix cores
+                                     (gdn_chunk_gated_delta_rule_fwd); either
+                                     layout; K, V in {32, 64, 128}; writes no
+                                     intermediate states; no tiling overrides  */
 
 /* Describes the launch that a configuration maps to (gdn_plan). */
 typedef struct gdn_launch_info {
-    int32_t kernel_family;    /* GDN_KERNEL_COLUMN_TILES or _ROW_SPLIT       */
+    int32_t kernel_family;    /* the GDN_KERNEL_* family that runs           */
     int32_t block_v;          /* V-columns per wavefront                     */
     int32_t block_k;          /* K-rows per wavefront                        */
     int32_t waves_per_group;  /* wavefronts per workgroup                    */
@@ -152,7 +158,7 @@ typedef struct gdn_launch_info {
     int32_t multi_token;      /* 0: single-token decode kernel; 1: token loop */
     int64_t workgroups;       /* grid size                                   */
     int32_t threads_per_group;
-    int32_t lds_bytes;        /* dynamic LDS per workgroup                   */
+    int32_t lds_bytes;        /* LDS per workgroup                           */
 } gdn_launch_info;
 
 /* Fills `cfg` with defaults: scale 0 (K^-1/2), eps 1e-6, dense strides,
@@ -213,6 +219,31 @@ gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, con
                                 const float* beta, void* state_pool, const int32_t* state_idx,
                                 const int32_t* cu_seqlens, void* out, void* intermediate_states,
                                 const gdn_config* cfg, void* stream);
+
+/*
+ * The chunked forward (prefill) of the same operation: the results of
+ * gdn_gating_delta_rule_update with intermediate_states = NULL (outputs and
+ * final states, up to fp32 rounding), computed 64 tokens at a time in the WY
+ * form of the chunked gated delta rule.  sglang PR #21411 (implementation
+ * section) fuses the chunk's K K^T, triangular solve and w/u recomputation
+ * (chunk_gated_delta_rule_fwd, CHUNK_SIZE 64); here one workgroup per
+ * (sequence, v-head) walks its chunks with the state resident on chip, so no
+ * chunk index table is needed.  Meant for long sequences: the work per chunk
+ * is dense matrix products, against one dependent step per token in the
+ * per-token kernels.
+ *
+ * Arguments, layouts, alignment and the caller contract are those of
+ * gdn_gating_delta_rule_update.  cfg->kernel_family must be GDN_KERNEL_AUTO
+ * or GDN_KERNEL_CHUNKED, and block_v, block_k and waves_per_group must be 0.
+ * K and V must be 32, 64 or 128, and 64 token rows of q, k, v or out must
+ * span less than 2 GiB.  gdn_recurrent_update with kernel_family =
+ * GDN_KERNEL_CHUNKED runs the same kernel on precomputed gates.
+ */
+gdn_status gdn_chunk_gated_delta_rule_fwd(
+    const void* q, const void* k, const void* v, const void* a, const void* b,
+    const float* A_log, const float* dt_bias, void* state_pool,
+    const int32_t* state_idx, const int32_t* cu_seqlens, void* out,
+    const gdn_config* cfg, void* stream);
 
 /* Host-side argument check of gdn_gating_delta_rule_update (same arguments,
  * no stream); launches nothing and never touches device memory. */

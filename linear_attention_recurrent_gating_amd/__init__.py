@@ -26,6 +26,7 @@ GDN_KERNEL_AUTO = 0
 GDN_KERNEL_COLUMN_TILES = 1
 GDN_KERNEL_ROW_SPLIT = 2
 GDN_KERNEL_VALUE_ROWS = 3
+GDN_KERNEL_CHUNKED = 4
 GDN_LAYOUT_KV = 0
 GDN_LAYOUT_VK = 1
 _LAYOUTS = {"KV": GDN_LAYOUT_KV, "VK": GDN_LAYOUT_VK, GDN_LAYOUT_KV: GDN_LAYOUT_KV,
@@ -37,7 +38,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_default_config", "gdn_gating_delta_rule_update", "gdn_gating",
-            "gdn_recurrent_update", "gdn_validate", "gdn_plan", "gdn_status_string",
+            "gdn_recurrent_update", "gdn_chunk_gated_delta_rule_fwd", "gdn_validate", "gdn_plan", "gdn_status_string",
             "gdn_last_error_message", "gdn_abi_version")
 
 
@@ -85,6 +86,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_gating.restype = ctypes.c_int
     lib.gdn_recurrent_update.argtypes = [P] * 10 + [C, P]
     lib.gdn_recurrent_update.restype = ctypes.c_int
+    lib.gdn_chunk_gated_delta_rule_fwd.argtypes = [P] * 11 + [C, P]
+    lib.gdn_chunk_gated_delta_rule_fwd.restype = ctypes.c_int
     lib.gdn_validate.argtypes = [P] * 12 + [C]
     lib.gdn_validate.restype = ctypes.c_int
     lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
@@ -273,6 +276,30 @@ def gdn_gating_delta_rule_update(q, k, v, a, b, A_log, dt_bias, state_pool, stat
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out),
         _ptr(intermediate_states), ctypes.byref(cfg), stream))
+    return out
+
+
+def gdn_chunk_gated_delta_rule_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx,
+                                   cu_seqlens=None, out=None, *, tokens_per_seq=None,
+                                   scale: float = 0.0, eps: float = 1e-6, flags: int = 0,
+                                   stream=None, state_layout=GDN_LAYOUT_KV):
+    """The chunked forward (64-token chunks on the matrix cores): the outputs
+    and final states of gdn_gating_delta_rule_update without intermediate
+    states.  Arguments as there; K and V must be 32, 64 or 128.  Returns ``out``."""
+    import torch
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out, None,
+                   state_layout)
+    cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
+                      scale=scale, eps=eps, flags=flags, k=k, state_layout=state_layout, a=a, b=b)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(raw_library().gdn_chunk_gated_delta_rule_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out), ctypes.byref(cfg), stream))
     return out
 
 

@@ -14,7 +14,7 @@ LIB = os.path.join(LIBDIR, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_INCLUDE = "/opt/rocm/include"
 
-DEVICE_SOURCES = ["gdn_kernels.hip"]
+DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_chunk.hip"]
 HOST_SOURCES = ["gdn_api.cpp"]
 
 # Packed fp32 VALU forms are disabled: hipcc -O3 otherwise forms them from

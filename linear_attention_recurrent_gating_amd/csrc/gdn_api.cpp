@@ -58,7 +58,8 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
     s.multi_token = (has_cu || c.tokens_per_seq > 1) ? 1 : 0;
     s.chunk = s.multi_token ? gdn::kChunkTokens : 1;
     if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_COLUMN_TILES &&
-        c.kernel_family != GDN_KERNEL_ROW_SPLIT && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
+        c.kernel_family != GDN_KERNEL_ROW_SPLIT && c.kernel_family != GDN_KERNEL_VALUE_ROWS &&
+        c.kernel_family != GDN_KERNEL_CHUNKED)
         return fail(GDN_ERR_BAD_ARGUMENT, "kernel_family = %d is not a GDN_KERNEL_* value",
                     c.kernel_family);
     if (c.waves_per_group < 0 || c.waves_per_group > 8)
@@ -67,6 +68,38 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
         return fail(GDN_ERR_BAD_ARGUMENT, "state_layout = %d is neither GDN_LAYOUT_KV nor _VK",
                     c.state_layout);
 
+    if (c.kernel_family == GDN_KERNEL_CHUNKED) {
+        if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "the chunked kernel takes no tiling overrides "
+                                              "(block_v, block_k, waves_per_group must be 0)");
+        const int bytes = gdn::chunk_lds_bytes(K, V, c.act_dtype);
+        if (bytes == 0)
+            return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no chunked kernel for K = %d, V = %d "
+                                                   "(each must be 32, 64 or 128)", K, V);
+        // Buffer offsets within one chunk are 32-bit.
+        const int64_t esize = c.act_dtype == GDN_DTYPE_F32 ? 4 : 2;
+        const int64_t rows[] = {c.q_stride_tok ? c.q_stride_tok : int64_t(c.num_k_heads) * K,
+                                c.k_stride_tok ? c.k_stride_tok : int64_t(c.num_k_heads) * K,
+                                c.v_stride_tok ? c.v_stride_tok : int64_t(c.num_v_heads) * V,
+                                int64_t(c.num_v_heads) * V};
+        for (int64_t r : rows)
+            if (r * esize * gdn::kChunkedTokens >= (int64_t(1) << 31))
+                return fail(GDN_ERR_UNSUPPORTED_SHAPE, "64 token rows of %lld elements exceed "
+                                                       "2 GiB", static_cast<long long>(r));
+        s.kind = gdn::kKindChunked;
+        s.multi_token = 1;
+        s.chunk = gdn::kChunkedTokens;
+        s.block_v = gdn::chunk_block_v();
+        s.block_k = K;
+        s.rows_rpl_max = 0;
+        s.waves = V / s.block_v;
+        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_v_heads;
+        if (s.groups > INT32_MAX)
+            return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
+                        static_cast<long long>(s.groups));
+        s.lds_bytes = bytes;
+        return GDN_OK;
+    }
     if (c.state_layout == GDN_LAYOUT_VK) {
         if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
             return fail(GDN_ERR_BAD_ARGUMENT, "GDN_LAYOUT_VK is served by GDN_KERNEL_VALUE_ROWS only");
@@ -304,6 +337,8 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
     }
     if (cu_seqlens && !aligned(cu_seqlens, 4))
         return fail(GDN_ERR_MISALIGNED, "cu_seqlens is not 4-byte aligned");
+    if (intermediate_states && cfg->kernel_family == GDN_KERNEL_CHUNKED)
+        return fail(GDN_ERR_BAD_ARGUMENT, "the chunked kernel writes no intermediate states");
     if (intermediate_states && !aligned(intermediate_states, state_align))
         return fail(GDN_ERR_MISALIGNED, "intermediate_states is not %zu-byte aligned", state_align);
     return GDN_OK;
@@ -361,6 +396,7 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
     p.eps = c.l2norm_eps;
     p.write_final = (c.flags & GDN_FLAG_NO_FINAL_WRITEBACK) ? 0 : 1;
     p.state_bf16 = c.state_dtype == GDN_DTYPE_BF16 ? 1 : 0;
+    p.state_vk = c.state_layout == GDN_LAYOUT_VK ? 1 : 0;
 
     static const bool log = [] {
         const char* e = std::getenv("GDN_LOG");
@@ -372,13 +408,15 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
                      "waves=%d chunk=%d groups=%lld lds=%d\n",
                      sh.kind == gdn::kKindRows        ? "rows"
                      : sh.kind == gdn::kKindValueRows ? "value-rows"
+                     : sh.kind == gdn::kKindChunked   ? "chunked"
                                                       : "columns",
                      sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", p.state_bf16 ? "bf16" : "f32",
                      g ? "precomputed" : "fused",
                      sh.multi_token, sh.block_v, sh.block_k, sh.waves, sh.chunk,
                      static_cast<long long>(sh.groups), sh.lds_bytes);
 
-    const hipError_t e = gdn::launch_fused(sh, p, st);
+    const hipError_t e = sh.kind == gdn::kKindChunked ? gdn::launch_chunked(sh, p, st)
+                                                      : gdn::launch_fused(sh, p, st);
     if (e != hipSuccess)
         return fail(GDN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
@@ -415,6 +453,7 @@ gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* 
     if (s != GDN_OK) return s;
     info->kernel_family = sh.kind == gdn::kKindRows        ? GDN_KERNEL_ROW_SPLIT
                           : sh.kind == gdn::kKindValueRows ? GDN_KERNEL_VALUE_ROWS
+                          : sh.kind == gdn::kKindChunked   ? GDN_KERNEL_CHUNKED
                                                            : GDN_KERNEL_COLUMN_TILES;
     info->block_k = sh.block_k;
     info->block_v = sh.block_v;
@@ -435,6 +474,22 @@ gdn_status gdn_gating_delta_rule_update(const void* q, const void* k, const void
                                         void* stream) {
     return run_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
                       cu_seqlens, out, intermediate_states, cfg, stream);
+}
+
+gdn_status gdn_chunk_gated_delta_rule_fwd(const void* q, const void* k, const void* v,
+                                          const void* a, const void* b, const float* A_log,
+                                          const float* dt_bias, void* state_pool,
+                                          const int32_t* state_idx, const int32_t* cu_seqlens,
+                                          void* out, const gdn_config* cfg, void* stream) {
+    g_last_error[0] = '\0';
+    if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
+    if (cfg->kernel_family != GDN_KERNEL_AUTO && cfg->kernel_family != GDN_KERNEL_CHUNKED)
+        return fail(GDN_ERR_BAD_ARGUMENT, "kernel_family = %d: the chunked forward runs "
+                                          "GDN_KERNEL_CHUNKED only", cfg->kernel_family);
+    gdn_config c = *cfg;
+    c.kernel_family = GDN_KERNEL_CHUNKED;
+    return run_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
+                      cu_seqlens, out, nullptr, &c, stream);
 }
 
 gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,

@@ -39,12 +39,14 @@ struct FusedParams {
     float eps;
     int32_t write_final;        // 0 under GDN_FLAG_NO_FINAL_WRITEBACK
     int32_t state_bf16;         // 1: pool and intermediates hold bf16
+    int32_t state_vk;           // 1: tiles stored transposed (V x K); chunked kernel only
 };
 
 // Kernel families.
 constexpr int kKindColumns = 0;  // wave = (v-head, BV-column tile); any token count
 constexpr int kKindRows = 1;     // wave = (v-head, block of whole rows); one token
 constexpr int kKindValueRows = 2;  // transposed (VK) state: wave = (v-head, block of value-rows)
+constexpr int kKindChunked = 3;    // workgroup = (sequence, v-head); 64-token chunks on MFMA
 
 struct LaunchShape {
     int kind;
@@ -81,6 +83,19 @@ int vk_rows_per_wave(int K, int V);
 hipError_t launch_gating(const void* a, const void* b, const float* A_log, const float* dt_bias,
                          float* g, float* beta, int64_t n, int Hv, int G, int64_t ab_stride,
                          int32_t ab_khead, int act, hipStream_t stream);
+
+// Static LDS bytes of the chunked kernel for (K, V, act); 0 if there is no
+// instance (K, V in {32, 64, 128}).
+int chunk_lds_bytes(int K, int V, int act);
+
+// Value columns per wavefront of the chunked kernel (V / this = wavefronts).
+int chunk_block_v();
+
+// Tokens per chunk of the chunked kernel.
+constexpr int kChunkedTokens = 64;
+
+// Enqueues the chunked kernel (grid = sequences x v-heads).
+hipError_t launch_chunked(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);
 
 // Enqueues the fused kernel; returns the HIP launch status.
 hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);

@@ -213,3 +213,25 @@ def algorithmic_bytes(inp: HostInputs, final_writeback: bool = True, state_bytes
     act = ntok * (2 * Hk * K * e + 2 * Hv * V * e + 2 * Hv * e)
     params = 8 * Hv + 4 * wl.num_seqs + (4 * (wl.num_seqs + 1) if wl.varlen else 0)
     return state + act + params
+
+
+CHUNK_TOKENS = 64  # tokens per chunk of the chunked forward
+
+
+def chunked_flops(inp: HostInputs, chunk: int = CHUNK_TOKENS) -> int:
+    """Flops of the dense products of the chunked (WY) form for every live
+    (sequence, v-head): per chunk of L tokens, the key-key and query-key
+    products (2 x 2 L^2 K), the products with the chunk-start state (2 x 2 L K V),
+    the triangular factor times R and the masked query-key matrix times U
+    (2 x 2 L^2 V), the state update (2 L K V) and the triangular inverse
+    (L^3 / 3 multiply-adds)."""
+    wl = inp.wl
+    K, V = wl.head_k_dim, wl.head_v_dim
+    total = 0
+    for L, s in zip(inp.lengths, inp.state_idx):
+        if s < 0:
+            continue
+        full, tail = divmod(int(L), chunk)
+        for n, c in ((full, chunk), (1 if tail else 0, tail)):
+            total += n * (4 * c * c * K + 4 * c * c * V + 6 * c * K * V + (2 * c ** 3) // 3)
+    return total * wl.num_v_heads

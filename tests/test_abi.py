@@ -98,7 +98,7 @@ def test_valid_config_passes():
     ("waves_per_group", 9, 7),
     ("waves_per_group", 3, 7),      # row split: not a multiple of the 4 waves per head
     ("kernel_family", 3, 7),        # value rows need the VK layout
-    ("kernel_family", 4, 7),
+    ("kernel_family", 5, 7),
     ("state_layout", 2, 7),
     ("block_k", 48, 7),             # no row-split kernel with 48 rows per wave
 ])
@@ -215,6 +215,54 @@ def test_plan_value_rows():
     big = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, head_k_dim=256,
                                 head_v_dim=256), False)
     assert big.block_v == 16 and big.waves_per_group == 8 and big.workgroups == 4 * 2 * 4
+
+
+def test_plan_chunked():
+    ck = gdn.gdn_plan(base_cfg(kernel_family=gdn.GDN_KERNEL_CHUNKED, tokens_per_seq=100,
+                               num_tokens=400), False)
+    assert ck.kernel_family == gdn.GDN_KERNEL_CHUNKED and ck.multi_token == 1
+    assert ck.tokens_per_chunk == 64 and ck.block_v == 16 and ck.block_k == 128
+    assert ck.waves_per_group == 8 and ck.workgroups == 4 * 4 and ck.threads_per_group == 512
+    assert 64 * 1024 < ck.lds_bytes <= 160 * 1024
+    # either layout and state dtype; V = 64 takes four wavefronts of 16 columns
+    vk = gdn.gdn_plan(base_cfg(kernel_family=gdn.GDN_KERNEL_CHUNKED, head_v_dim=64,
+                               state_layout=gdn.GDN_LAYOUT_VK, state_dtype=gdn.GDN_DTYPE_BF16),
+                      True)
+    assert vk.kernel_family == gdn.GDN_KERNEL_CHUNKED and vk.waves_per_group == 4
+    f32 = gdn.gdn_plan(base_cfg(kernel_family=gdn.GDN_KERNEL_CHUNKED,
+                                act_dtype=gdn.GDN_DTYPE_F32), False)
+    assert f32.lds_bytes <= 160 * 1024
+    chunked = dict(kernel_family=gdn.GDN_KERNEL_CHUNKED)
+    assert validate(base_cfg(head_k_dim=256, **chunked)) == 3
+    assert validate(base_cfg(head_v_dim=256, **chunked)) == 3
+    for over in ("block_v", "block_k", "waves_per_group"):
+        assert validate(base_cfg(**{over: 32 if over != "waves_per_group" else 4}, **chunked)) == 7
+    # no per-token states
+    assert validate(base_cfg(**chunked), inter=A[11]) == 7
+    assert validate(base_cfg(**chunked)) == 0
+    # 64 rows of a 2^25-element token stride (bf16) span 4 GiB: offsets would overflow
+    assert validate(base_cfg(k_stride_tok=1 << 25, **chunked)) == 3
+    # AUTO never picks the chunked kernel, even for long sequences
+    auto = gdn.gdn_plan(base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096), False)
+    assert auto.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+
+
+def test_chunked_entry_point_validation():
+    lib = gdn.raw_library()
+    c = base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT)
+    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ctypes.byref(c),
+                                              None) == 7
+    c = base_cfg(head_k_dim=256)
+    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ctypes.byref(c),
+                                              None) == 3
+    c = base_cfg()
+    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, None, ctypes.byref(c),
+                                              None) == 1
+    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], None, None) == 1
+    # a zero-sequence batch returns before touching anything
+    c = base_cfg(num_seqs=0, num_tokens=0)
+    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ctypes.byref(c),
+                                              None) == 0
 
 
 def test_ab_stride_validation():
