@@ -183,6 +183,24 @@ __device__ __forceinline__ void buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t 
     }
 }
 
+// Inclusive prefix sum over the 64 lanes: a Hillis-Steele scan inside each
+// 16-lane row (row_shr 1, 2, 4, 8; lanes shifted in from outside the row add
+// 0), then the row totals carried down with row_bcast:15 and row_bcast:31.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+    x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+    x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+    x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+    x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 // LDS written by some lanes of this wavefront becomes visible to its others.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -192,14 +210,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Staging loads of one chunk, issued a chunk ahead so that they land while
 // the previous chunk's products run: raw keys and queries (16-byte vectors,
-// NQK per lane), this wave's v values in accumulator order, and the raw gate
-// inputs of token `lane` (wave 0).
+// NQK per lane) and the raw gate inputs of token `lane` (wave 0).
 template <int ACT, int NQK>
 struct ChunkLoads {
     static constexpr int VEC = ACT == 0 ? 2 : 1;   // 16-byte vectors per 8 elements
     u32x4v k[NQK][VEC];
     u32x4v q[NQK][VEC];
-    float v[4][kNT][4];
     float ga, gb;
 };
 
@@ -313,33 +329,19 @@ gdn_chunk_fwd(const FusedParams p) {
                                     (Ln - 1) * krow + K * esz);
         const auto qr = buffer_rsrc(static_cast<const char*>(p.q) + (u0 * p.q_stride + int64_t(j) * K) * esz,
                                     (Ln - 1) * qrow + K * esz);
-        const auto vr = buffer_rsrc(static_cast<const char*>(p.v) + (u0 * p.v_stride + int64_t(h) * V) * esz,
-                                    (Ln - 1) * vrow + V * esz);
+        // Vectors past the chunk (vi >= C * CPL, only when the workgroup
+        // does not divide the chunk evenly) fall outside the resources and
+        // load as zero; there is no branch, so no wait is forced here.
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
             const int vi = tid + i * Pl::THREADS;
-            if (vi < kC * CPL) {
-                const int t = vi / CPL, c8 = vi % CPL;
+            const int t = vi / CPL, c8 = vi % CPL;
 #pragma unroll
-                for (int h2 = 0; h2 < ChunkLoads<ACT, NQK>::VEC; ++h2) {
-                    L.k[i][h2] = __builtin_amdgcn_raw_buffer_load_b128(kr, t * krow + (8 * c8 * esz + 16 * h2), 0, 0);
-                    L.q[i][h2] = __builtin_amdgcn_raw_buffer_load_b128(qr, t * qrow + (8 * c8 * esz + 16 * h2), 0, 0);
-                }
+            for (int h2 = 0; h2 < ChunkLoads<ACT, NQK>::VEC; ++h2) {
+                L.k[i][h2] = __builtin_amdgcn_raw_buffer_load_b128(kr, t * krow + (8 * c8 * esz + 16 * h2), 0, 0);
+                L.q[i][h2] = __builtin_amdgcn_raw_buffer_load_b128(qr, t * qrow + (8 * c8 * esz + 16 * h2), 0, 0);
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int ct = 0; ct < kNT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t su = (16 * r + e) * vrow + 16 * ct * esz;
-                    if constexpr (ACT == 0)
-                        L.v[r][ct][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, act_lane, su, 0));
-                    else
-                        L.v[r][ct][e] = __uint_as_float(
-                            uint32_t(__builtin_amdgcn_raw_buffer_load_b16(vr, act_lane, su, 0)) << 16);
-                }
         // Gate inputs of token `lane` (wave 0); rows past the chunk load as 0.
         if (wave == 0) {
             if (p.g) {
@@ -366,15 +368,14 @@ gdn_chunk_fwd(const FusedParams p) {
 
     // Stage chunk cn from its loads: raw keys and queries into LDS (bf16
     // parts), their inverse norms, the gates and the prefix sums of the
-    // log-decays (scalar buffer cn & 1), and this wave's v values.
-    float vnext[4][kNT][4];
+    // log-decays (scalar buffer cn & 1).
     auto stage = [&](int cn, const ChunkLoads<ACT, NQK>& L) {
         const int Ln = chunk_len(cn);
         float* const sc = scal + (cn & 1) * Pl::kScalars * kC;
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
             const int vi = tid + i * Pl::THREADS;
-            if (vi < kC * CPL) {
+            if ((kC * CPL) % Pl::THREADS == 0 || vi < kC * CPL) {
                 const int t = vi / CPL, c8 = vi % CPL;
                 float xk[8], xq[8];
 #pragma unroll
@@ -425,12 +426,6 @@ gdn_chunk_fwd(const FusedParams p) {
                 }
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int ct = 0; ct < kNT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vnext[r][ct][e] = L.v[r][ct][e];
         if (wave == 0) {
             float glog, bet;
             if (p.g) {
@@ -440,13 +435,8 @@ gdn_chunk_fwd(const FusedParams p) {
                 gate_values(L.ga, L.gb, A_h, dtb_h, glog, bet);
             }
             if (lane >= Ln) glog = bet = 0.0f;  // padding tokens: no decay, no update
-            float G = glog;
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                const float y = __shfl_up(G, d);
-                if (lane >= d) G += y;
-            }
-            const float Glast = __shfl(G, kWave - 1);
+            const float G = wave_prefix_sum(glog);
+            const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kWave - 1));
             sc[lane] = bet;
             sc[5 * kC + lane] = G;
             sc[kC + lane] = expf(G);
@@ -472,22 +462,36 @@ gdn_chunk_fwd(const FusedParams p) {
         const float* const s_rk = sc + 3 * kC;
         const float* const s_rq = sc + 4 * kC;
         const float* const s_G = sc + 5 * kC;
-        float vv[4][kNT][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int ct = 0; ct < kNT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vv[r][ct][e] = vnext[r][ct][e];
         lds_barrier();  // chunk c is staged; the previous chunk's products are done
+        // This wave's v values (accumulator row order), needed once the
+        // state products are done; they land during the Gram tiles.
+        float vv[4][kNT][4];
+        {
+            const auto vr = buffer_rsrc(static_cast<const char*>(p.v) + (t0 * p.v_stride + int64_t(h) * V) * esz,
+                                        (Lc - 1) * vrow + V * esz);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int ct = 0; ct < kNT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t su = (16 * r + e) * vrow + 16 * ct * esz;
+                        if constexpr (ACT == 0)
+                            vv[r][ct][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, act_lane, su, 0));
+                        else
+                            vv[r][ct][e] = __uint_as_float(
+                                uint32_t(__builtin_amdgcn_raw_buffer_load_b16(vr, act_lane, su, 0)) << 16);
+                    }
+        }
 
         // ------------------------------------------ B: Gram tiles, D_b = (I + L_bb)^-1
-        // 20 tiles: K K^T on and below the diagonal (L), then Q K^T on and
-        // below it (P).  Tile w of wave w (w < 4) is the diagonal block w,
-        // which the same wave then inverts.
-        for (int task = wave; task < 20; task += NW) {
-            const bool isq = task >= 10;
-            int ti, tj;
+        // 20 tiles: the 4 diagonal blocks of K K^T (then inverted), the 6
+        // below them (L), and the 10 of Q K^T on and below the diagonal (P).
+        // With 8 or more wavefronts, wavefronts 0-3 take one diagonal block
+        // each and 4-7 share the other 16 tiles; otherwise tiles are dealt
+        // round-robin.
+        auto tile_of = [](int task, bool& isq, int& ti, int& tj) {
+            isq = task >= 10;
             if (task < 4) {
                 ti = tj = task;
             } else if (!isq) {  // strictly below the diagonal: (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
@@ -499,21 +503,10 @@ gdn_chunk_fwd(const FusedParams p) {
                 ti = o >= 6 ? 3 : o >= 3 ? 2 : o >= 1 ? 1 : 0;
                 tj = o - ti * (ti + 1) / 2;
             }
-            const __bf16* xa = (isq ? qt : kt) + (16 * ti + m16) * KT + 8 * g4;
-            const __bf16* xb = kt + (16 * tj + m16) * KT + 8 * g4;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 a = lds_row8(xa + 32 * kb);
-                const bf16x8 b = lds_row8(xb + 32 * kb);
-                acc = mma_bf16(a, b, acc);
-                if constexpr (P == 2) {
-                    const bf16x8 al = lds_row8(xa + kC * KT + 32 * kb);
-                    const bf16x8 bl = lds_row8(xb + kC * KT + 32 * kb);
-                    acc = mma_bf16(a, bl, acc);
-                    acc = mma_bf16(al, b, acc);
-                }
-            }
+        };
+        // Scales the tile (X K^T)[16 ti.., 16 tj..] held in acc into P (X = Q),
+        // the fp32 diagonal block of L, or -L below the diagonal blocks.
+        auto tile_epilogue = [&](bool isq, int ti, int tj, const f32x4& acc) {
             // acc[e] = (X K^T)[16 ti + 4 g4 + e][16 tj + m16]
             const int s = 16 * tj + m16;
             const float rks = s_rk[s], Gs = s_G[s];
@@ -542,22 +535,33 @@ gdn_chunk_fwd(const FusedParams p) {
                     tb[kC * KC + t * KC + s] = lo;
                 }
             }
-            if (task < 4) {
-                // D_b = (I + L_bb)^-1 by forward substitution: column m16, the
-                // dot products split over the four lane groups.
-                wave_lds_sync();
+        };
+        // D_b = (I + L_bb)^-1 from the diagonal block written by this wavefront.
+        auto invert_diag = [&](int ti) {
+                // D_b = (I + L_bb)^-1 by forward substitution on column m16,
+                // four rows at a time: the dot products with the solved rows
+                // of earlier quads are split over the four lane groups and
+                // summed with two swaps; the quad's own rows follow locally.
                 const float* Lb = lt + ti * 16 * LD;
-                // Lane group g4 keeps y[q] = x[4 q + g4]; entries not yet
-                // solved are 0, and so is L on and above its diagonal.
-                float y[4] = {0.f, 0.f, 0.f, 0.f};
+                float y[4] = {0.f, 0.f, 0.f, 0.f};   // y[q] = x[4 q + g4]
 #pragma unroll
-                for (int ii = 0; ii < 16; ++ii) {
-                    float part = 0.0f;
+                for (int pq = 0; pq < 4; ++pq) {
+                    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (4 * q < ii) part = __builtin_fmaf(Lb[ii * LD + 4 * q + g4], y[q], part);
-                    const float xi = (ii == m16 ? 1.0f : 0.0f) - sum_xor32(sum_xor16(part));
-                    if (ii % 4 == g4) y[ii / 4] = xi;
+                    for (int q = 0; q < pq; ++q)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            part[i] = __builtin_fmaf(Lb[(4 * pq + i) * LD + 4 * q + g4], y[q], part[i]);
+                    float xq[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = (4 * pq + i == m16 ? 1.0f : 0.0f) - sum_xor32(sum_xor16(part[i]));
+#pragma unroll
+                        for (int i2 = 0; i2 < i; ++i2)
+                            v = __builtin_fmaf(-Lb[(4 * pq + i) * LD + 4 * pq + i2], xq[i2], v);
+                        xq[i] = v;
+                    }
+                    y[pq] = g4 == 0 ? xq[0] : g4 == 1 ? xq[1] : g4 == 2 ? xq[2] : xq[3];
                 }
                 const int b0 = 16 * ti;
 #pragma unroll
@@ -567,7 +571,44 @@ gdn_chunk_fwd(const FusedParams p) {
                     tb[(b0 + 4 * q + g4) * KC + b0 + m16] = hi;
                     tb[kC * KC + (b0 + 4 * q + g4) * KC + b0 + m16] = lo;
                 }
+        };
+        // (X K^T) tile products on bf16 MFMA (split parts for fp32 inputs).
+        auto tile_product = [&](const __bf16* xa, const __bf16* xb, f32x4& acc, int kb) {
+            const bf16x8 av = lds_row8(xa + 32 * kb);
+            const bf16x8 bv = lds_row8(xb + 32 * kb);
+            acc = mma_bf16(av, bv, acc);
+            if constexpr (P == 2) {
+                const bf16x8 al = lds_row8(xa + kC * KT + 32 * kb);
+                const bf16x8 bl = lds_row8(xb + kC * KT + 32 * kb);
+                acc = mma_bf16(av, bl, acc);
+                acc = mma_bf16(al, bv, acc);
             }
+        };
+        auto gram_tile = [&](int task) {
+            bool isq;
+            int ti, tj;
+            tile_of(task, isq, ti, tj);
+            const __bf16* xa = (isq ? qt : kt) + (16 * ti + m16) * KT + 8 * g4;
+            const __bf16* xb = kt + (16 * tj + m16) * KT + 8 * g4;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) tile_product(xa, xb, acc, kb);
+            tile_epilogue(isq, ti, tj, acc);
+            if (task < 4) {
+                wave_lds_sync();
+                invert_diag(ti);
+            }
+        };
+        if (NW >= 8) {
+            // Eight wavefronts: wavefronts 4-7 take one diagonal block each
+            // (and invert it), and every wavefront takes two of the other 16
+            // tiles.
+            if (wave >= 4) gram_tile(wave - 4);
+#pragma unroll 1
+            for (int task = 4 + wave; task < 20; task += 8) gram_tile(task);
+        } else {
+#pragma unroll 1
+            for (int task = wave; task < 20; task += NW) gram_tile(task);
         }
         // -------------------------------- C: products with the chunk-start state
         // Keys transposed to [K][C] for the state update (token pairs per lane).
