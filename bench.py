@@ -315,14 +315,13 @@ def main():
     updates = W.active_updates(inp)
     alg_bytes = W.algorithmic_bytes(inp, state_bytes=2 if args.state_dtype == "bf16" else 4)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    chunked = args.family == gdn.GDN_KERNEL_CHUNKED
     value = updates * args.steps / wall
     info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
                                         tokens_per_seq=wl.tokens_per_seq,
                                         kernel_family=args.family, block_v=args.block_v,
                                         block_k=args.block_k, waves_per_group=args.waves,
                                         state_layout=args.layout),
-                        d["cu_seqlens"] is not None)
+                        d["cu_seqlens"] is not None, inter is not None)
 
     res = {
         "metric": METRIC,
@@ -357,7 +356,7 @@ def main():
                      "algorithmic_bytes": alg_bytes, "kernel": KERNEL_NAMES[info.kernel_family]},
         "cpu_baseline": None,
     }
-    if chunked:
+    if info.kernel_family == gdn.GDN_KERNEL_CHUNKED:
         # Dense products of the chunked form on the bf16 matrix cores.
         flops = W.chunked_flops(inp)
         tflops = flops / (kern_ms * 1e-3) / 1e12

@@ -119,10 +119,12 @@ typedef struct gdn_config {
                                 on store (half the state traffic)              */
     /* Tiling overrides (0 = the library's static table).  They change the
      * order of the fp32 reductions, never the operation. */
-    int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): with GDN_LAYOUT_KV, row split
-                                for one token per sequence and column tiles
-                                otherwise; with GDN_LAYOUT_VK, value rows.
-                                GDN_KERNEL_CHUNKED is never chosen by AUTO     */
+    int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): the chunked kernel for
+                                calls without intermediate states averaging at
+                                least 32 tokens per sequence (K, V <= 128);
+                                otherwise, with GDN_LAYOUT_KV, row split for
+                                one token per sequence and column tiles for
+                                more; with GDN_LAYOUT_VK, value rows           */
     int32_t block_v;         /* column tiles: 8, 16, 32 or 64 V-columns per
                                 wavefront (dividing V).  A non-zero value with
                                 GDN_KERNEL_AUTO selects the column tiles        */
@@ -253,8 +255,9 @@ gdn_status gdn_validate(
     const int32_t* state_idx, const int32_t* cu_seqlens, const void* out,
     const void* intermediate_states, const gdn_config* cfg);
 
-/* The launch a valid configuration maps to (no device access). */
-gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens,
+/* The launch a valid configuration maps to (no device access), for a call
+ * with or without cu_seqlens and intermediate_states. */
+gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, int has_intermediate_states,
                     gdn_launch_info* info);
 
 /* Static description of a status code (never NULL). */

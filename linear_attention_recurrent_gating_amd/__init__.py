@@ -90,7 +90,7 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_gated_delta_rule_fwd.restype = ctypes.c_int
     lib.gdn_validate.argtypes = [P] * 12 + [C]
     lib.gdn_validate.restype = ctypes.c_int
-    lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
+    lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
     lib.gdn_plan.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -387,8 +387,9 @@ def gdn_validate(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlen
                              _ptr(out), _ptr(intermediate_states), ctypes.byref(cfg))
 
 
-def gdn_plan(cfg: GdnConfig, has_cu_seqlens: bool) -> GdnLaunchInfo:
+def gdn_plan(cfg: GdnConfig, has_cu_seqlens: bool, has_intermediates: bool = False) -> GdnLaunchInfo:
     info = GdnLaunchInfo()
-    _check(raw_library().gdn_plan(ctypes.byref(cfg), int(bool(has_cu_seqlens)), ctypes.byref(info)))
+    _check(raw_library().gdn_plan(ctypes.byref(cfg), int(bool(has_cu_seqlens)),
+                                  int(bool(has_intermediates)), ctypes.byref(info)))
     return info
 

@@ -45,12 +45,63 @@ int default_waves(int units) {
     return 1;
 }
 
+// The chunked kernel's launch for a config, or the reason it has none.
+gdn_status chunked_shape(const gdn_config& c, gdn::LaunchShape& s) {
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0)
+        return fail(GDN_ERR_BAD_ARGUMENT, "the chunked kernel takes no tiling overrides "
+                                          "(block_v, block_k, waves_per_group must be 0)");
+    const int bytes = gdn::chunk_lds_bytes(K, V, c.act_dtype);
+    if (bytes == 0)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no chunked kernel for K = %d, V = %d "
+                                               "(each must be 32, 64 or 128)", K, V);
+    // Buffer offsets within one chunk are 32-bit.
+    const int64_t esize = c.act_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    const int64_t rows[] = {c.q_stride_tok ? c.q_stride_tok : int64_t(c.num_k_heads) * K,
+                            c.k_stride_tok ? c.k_stride_tok : int64_t(c.num_k_heads) * K,
+                            c.v_stride_tok ? c.v_stride_tok : int64_t(c.num_v_heads) * V,
+                            int64_t(c.num_v_heads) * V};
+    for (int64_t r : rows)
+        if (r * esize * gdn::kChunkedTokens >= (int64_t(1) << 31))
+            return fail(GDN_ERR_UNSUPPORTED_SHAPE, "64 token rows of %lld elements exceed 2 GiB",
+                        static_cast<long long>(r));
+    s.kind = gdn::kKindChunked;
+    s.multi_token = 1;
+    s.chunk = gdn::kChunkedTokens;
+    s.block_v = gdn::chunk_block_v();
+    s.block_k = K;
+    s.rows_rpl_max = 0;
+    s.waves = V / s.block_v;
+    s.groups = static_cast<int64_t>(c.num_seqs) * c.num_v_heads;
+    if (s.groups > INT32_MAX)
+        return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
+                    static_cast<long long>(s.groups));
+    s.lds_bytes = bytes;
+    return GDN_OK;
+}
+
+// GDN_KERNEL_AUTO takes the chunked kernel for calls that write no
+// intermediate states and average at least kChunkedMinMeanTokens tokens per
+// sequence (measured on MI355X: from 32 tokens on, its 64-token chunks beat
+// the per-token loop), when it has an instance for the shape.
+constexpr int64_t kChunkedMinMeanTokens = 32;
+
+bool auto_chunked(const gdn_config& c, bool has_inter) {
+    if (c.kernel_family != GDN_KERNEL_AUTO || has_inter) return false;
+    if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0) return false;
+    if (c.num_seqs <= 0 || c.num_tokens < kChunkedMinMeanTokens * c.num_seqs) return false;
+    gdn::LaunchShape probe{};
+    const bool ok = chunked_shape(c, probe) == GDN_OK;
+    g_last_error[0] = '\0';
+    return ok;
+}
+
 // Chooses the kernel family, tile and grid of a (size-checked) config, and
 // rejects tiling overrides that have no kernel instance.  Single-token calls
 // default to the row-split kernel (one contiguous kilobyte per load/store
 // instruction); multi-token calls, and calls that override block_v, use the
 // column-tile kernel.
-gdn_status plan_launch(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
+gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::LaunchShape& s) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
     s.K = K;
@@ -68,38 +119,8 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
         return fail(GDN_ERR_BAD_ARGUMENT, "state_layout = %d is neither GDN_LAYOUT_KV nor _VK",
                     c.state_layout);
 
-    if (c.kernel_family == GDN_KERNEL_CHUNKED) {
-        if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0)
-            return fail(GDN_ERR_BAD_ARGUMENT, "the chunked kernel takes no tiling overrides "
-                                              "(block_v, block_k, waves_per_group must be 0)");
-        const int bytes = gdn::chunk_lds_bytes(K, V, c.act_dtype);
-        if (bytes == 0)
-            return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no chunked kernel for K = %d, V = %d "
-                                                   "(each must be 32, 64 or 128)", K, V);
-        // Buffer offsets within one chunk are 32-bit.
-        const int64_t esize = c.act_dtype == GDN_DTYPE_F32 ? 4 : 2;
-        const int64_t rows[] = {c.q_stride_tok ? c.q_stride_tok : int64_t(c.num_k_heads) * K,
-                                c.k_stride_tok ? c.k_stride_tok : int64_t(c.num_k_heads) * K,
-                                c.v_stride_tok ? c.v_stride_tok : int64_t(c.num_v_heads) * V,
-                                int64_t(c.num_v_heads) * V};
-        for (int64_t r : rows)
-            if (r * esize * gdn::kChunkedTokens >= (int64_t(1) << 31))
-                return fail(GDN_ERR_UNSUPPORTED_SHAPE, "64 token rows of %lld elements exceed "
-                                                       "2 GiB", static_cast<long long>(r));
-        s.kind = gdn::kKindChunked;
-        s.multi_token = 1;
-        s.chunk = gdn::kChunkedTokens;
-        s.block_v = gdn::chunk_block_v();
-        s.block_k = K;
-        s.rows_rpl_max = 0;
-        s.waves = V / s.block_v;
-        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_v_heads;
-        if (s.groups > INT32_MAX)
-            return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
-                        static_cast<long long>(s.groups));
-        s.lds_bytes = bytes;
-        return GDN_OK;
-    }
+    if (c.kernel_family == GDN_KERNEL_CHUNKED || auto_chunked(c, has_inter))
+        return chunked_shape(c, s);
     if (c.state_layout == GDN_LAYOUT_VK) {
         if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
             return fail(GDN_ERR_BAD_ARGUMENT, "GDN_LAYOUT_VK is served by GDN_KERNEL_VALUE_ROWS only");
@@ -207,7 +228,7 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, gdn::LaunchShape& s) {
     return GDN_OK;
 }
 
-gdn_status check_config(const gdn_config* cfg, bool has_cu) {
+gdn_status check_config(const gdn_config* cfg, bool has_cu, bool has_inter) {
     if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
     const gdn_config& c = *cfg;
     if (c.num_seqs < 0) return fail(GDN_ERR_BAD_SHAPE, "num_seqs = %d < 0", c.num_seqs);
@@ -255,7 +276,7 @@ gdn_status check_config(const gdn_config* cfg, bool has_cu) {
                         static_cast<long long>(st.s));
     }
     gdn::LaunchShape sh{};
-    return plan_launch(c, has_cu, sh);
+    return plan_launch(c, has_cu, has_inter, sh);
 }
 
 gdn_status debug_check_indices(const gdn_config& c, const int32_t* state_idx,
@@ -315,7 +336,7 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
                            const int32_t* cu_seqlens, const void* out,
                            const void* intermediate_states, const gdn_config* cfg) {
     g_last_error[0] = '\0';
-    gdn_status s = check_config(cfg, cu_seqlens != nullptr);
+    gdn_status s = check_config(cfg, cu_seqlens != nullptr, intermediate_states != nullptr);
     if (s != GDN_OK) return s;
     s = check_ab_strides(*cfg);
     if (s != GDN_OK) return s;
@@ -360,7 +381,7 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
     }
     const bool has_cu = cu_seqlens != nullptr;
     gdn::LaunchShape sh{};
-    s = plan_launch(c, has_cu, sh);
+    s = plan_launch(c, has_cu, intermediate_states != nullptr, sh);
     if (s != GDN_OK) return s;
 
     gdn::FusedParams p{};
@@ -443,13 +464,14 @@ gdn_status gdn_validate(const void* q, const void* k, const void* v, const void*
                            cu_seqlens, out, intermediate_states, cfg);
 }
 
-gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, gdn_launch_info* info) {
+gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, int has_intermediate_states,
+                    gdn_launch_info* info) {
     g_last_error[0] = '\0';
     if (!info) return fail(GDN_ERR_NULL_POINTER, "info is NULL");
-    gdn_status s = check_config(cfg, has_cu_seqlens != 0);
+    gdn_status s = check_config(cfg, has_cu_seqlens != 0, has_intermediate_states != 0);
     if (s != GDN_OK) return s;
     gdn::LaunchShape sh{};
-    s = plan_launch(*cfg, has_cu_seqlens != 0, sh);
+    s = plan_launch(*cfg, has_cu_seqlens != 0, has_intermediate_states != 0, sh);
     if (s != GDN_OK) return s;
     info->kernel_family = sh.kind == gdn::kKindRows        ? GDN_KERNEL_ROW_SPLIT
                           : sh.kind == gdn::kKindValueRows ? GDN_KERNEL_VALUE_ROWS

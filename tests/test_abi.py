@@ -242,9 +242,22 @@ def test_plan_chunked():
     assert validate(base_cfg(**chunked)) == 0
     # 64 rows of a 2^25-element token stride (bf16) span 4 GiB: offsets would overflow
     assert validate(base_cfg(k_stride_tok=1 << 25, **chunked)) == 3
-    # AUTO never picks the chunked kernel, even for long sequences
-    auto = gdn.gdn_plan(base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096), False)
-    assert auto.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    # AUTO takes the chunked kernel from 32 tokens per sequence on average,
+    # unless intermediate states are written or a tiling override is given
+    long = base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096)
+    assert gdn.gdn_plan(long, False).kernel_family == gdn.GDN_KERNEL_CHUNKED
+    assert gdn.gdn_plan(long, False, True).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    assert gdn.gdn_plan(base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096, block_v=32),
+                        False).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    at32 = base_cfg(tokens_per_seq=32, num_tokens=4 * 32)
+    assert gdn.gdn_plan(at32, False).kernel_family == gdn.GDN_KERNEL_CHUNKED
+    below = base_cfg(tokens_per_seq=31, num_tokens=4 * 31)
+    assert gdn.gdn_plan(below, False).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    # varlen: the mean length decides (num_tokens / num_seqs)
+    assert gdn.gdn_plan(base_cfg(num_tokens=4 * 40), True).kernel_family == gdn.GDN_KERNEL_CHUNKED
+    # no chunked instance for K = 256: AUTO falls back without an error
+    big = gdn.gdn_plan(base_cfg(head_k_dim=256, tokens_per_seq=100, num_tokens=400), False)
+    assert big.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and gdn.gdn_last_error_message() == ""
 
 
 def test_chunked_entry_point_validation():

@@ -164,12 +164,18 @@ def test_spec_verify_weak_decay(dev):
     full_check(W.SPEC_VERIFY.with_(name="spec_verify_weak", decay="weak", seed=44), dev)
 
 
-def test_varlen_long(dev):
-    full_check(W.VARLEN_LONG, dev)
+@pytest.mark.parametrize("family", [0, 1], ids=["auto_chunked", "column_tiles"])
+def test_varlen_long(dev, family):
+    """The long-varlen workload: AUTO takes the chunked kernel there (no
+    intermediate states, long sequences); the per-token column-tile kernel
+    is checked on it too."""
+    full_check(W.VARLEN_LONG, dev, family=family)
 
 
-def test_varlen_long_weak_decay(dev):
-    full_check(W.VARLEN_LONG.with_(name="varlen_long_weak", decay="weak", seed=45), dev)
+@pytest.mark.parametrize("family", [0, 1], ids=["auto_chunked", "column_tiles"])
+def test_varlen_long_weak_decay(dev, family):
+    full_check(W.VARLEN_LONG.with_(name="varlen_long_weak", decay="weak", seed=45), dev,
+               family=family)
 
 
 @pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
@@ -260,11 +266,12 @@ def test_deterministic(dev):
     wl = W.VARLEN_LONG.with_(name="det", num_seqs=3, len_range=(20, 70), seed=51)
     inp = W.make_host_inputs(wl)
     pool_np = W.make_pool_host(wl)
-    p1 = torch.from_numpy(pool_np).to(dev)
-    p2 = torch.from_numpy(pool_np).to(dev)
-    o1, _ = run_gpu(inp, p1, dev)
-    o2, _ = run_gpu(inp, p2, dev)
-    assert torch.equal(o1.nan_to_num(), o2.nan_to_num()) and torch.equal(p1, p2)
+    for family in (0, 1):   # chunked under AUTO (mean length >= 32), column tiles
+        p1 = torch.from_numpy(pool_np).to(dev)
+        p2 = torch.from_numpy(pool_np).to(dev)
+        o1, _ = run_gpu(inp, p1, dev, kernel_family=family)
+        o2, _ = run_gpu(inp, p2, dev, kernel_family=family)
+        assert torch.equal(o1.nan_to_num(), o2.nan_to_num()) and torch.equal(p1, p2)
 
 
 def test_strided_views_match_dense(dev):
@@ -397,7 +404,9 @@ def test_vk_all_head_dims(dev, K, V):
                                 W.SPEC_VERIFY.with_(name="spec_verify_weak_vk", decay="weak", seed=46)],
                          ids=lambda w: w.name)
 def test_vk_workloads(dev, wl):
-    full_check(wl, dev, layout="VK")
+    """The value-row kernel on the named workloads (chosen explicitly: AUTO
+    takes the chunked kernel for the long-varlen one)."""
+    full_check(wl, dev, layout="VK", family=3)
 
 
 @pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
