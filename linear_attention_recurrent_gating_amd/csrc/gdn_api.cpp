@@ -166,14 +166,28 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
     }
 
     if (rows) {
-        int rpl_max = 16;
+        // 8 state rows per lane where that instance exists (measured faster
+        // on MI355X than 16: more, smaller workgroups), unless a block_k or
+        // waves_per_group override asks for the other.
+        int rpl_max = 0;
         if (c.block_k != 0) {
-            rpl_max = 0;
             for (int r : {16, 8})
                 if (gdn::rows_per_wave(K, V, r) == c.block_k) { rpl_max = r; break; }
             if (!rpl_max)
                 return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
                                                   "wavefront for K = %d, V = %d", c.block_k, K, V);
+        } else {
+            for (int r : {8, 16}) {
+                const int rpw = gdn::rows_per_wave(K, V, r);
+                if (rpw == 0) continue;
+                const int kw = K / rpw;
+                if (c.waves_per_group != 0 &&
+                    (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0))
+                    continue;
+                rpl_max = r;
+                break;
+            }
+            if (!rpl_max) rpl_max = 16;   // reported below
         }
         const int rpw = gdn::rows_per_wave(K, V, rpl_max);
         if (rpw == 0)

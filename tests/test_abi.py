@@ -160,8 +160,9 @@ def test_plan_tile_table():
     assert decode.multi_token == 0 and decode.tokens_per_chunk == 1
     assert decode.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     assert decode.block_v == 128                   # whole rows per wavefront
+    assert decode.block_k == 16                    # 8 rows per lane: 8 waves per head
     assert decode.waves_per_group == 8 and decode.threads_per_group == 512
-    assert decode.workgroups == 512 * 16          # one per (sequence, k-head)
+    assert decode.workgroups == 512 * 32          # one per (sequence, v-head)
     assert decode.lds_bytes == (2 * 128 + 8 * (2 * 128 + 4)) * 4
     # K = V = 256 would need 16 row blocks per head: the column-tile kernel takes it
     big = gdn.gdn_plan(base_cfg(head_k_dim=256, head_v_dim=256), False)
@@ -175,10 +176,13 @@ def test_plan_tile_table():
     # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
     odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32), True)
     assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
-    # row split with G = 3, K = V = 128: 4 waves per head, one head per group
+    # row split with G = 3, K = V = 128: 8 waves per head, one head per group
     odd_rows = gdn.gdn_plan(base_cfg(num_v_heads=6), False)
     assert odd_rows.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
-    assert odd_rows.waves_per_group == 4 and odd_rows.workgroups == 4 * 2 * 3
+    assert odd_rows.waves_per_group == 8 and odd_rows.workgroups == 4 * 2 * 3
+    # 16 rows per lane when asked for four waves per workgroup
+    odd4 = gdn.gdn_plan(base_cfg(num_v_heads=6, waves_per_group=4), False)
+    assert odd4.block_k == 32 and odd4.workgroups == 4 * 2 * 3
     forced = gdn.gdn_plan(base_cfg(block_v=16, waves_per_group=4), False)
     assert forced.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
     assert forced.block_v == 16 and forced.waves_per_group == 4 and forced.block_k == 128
