@@ -31,9 +31,11 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 int default_block_v(const gdn_config& c) {
-    // One 128-byte line per row segment: 32 fp32 columns, the widest tile
-    // whose K x BV slice stays at 64 VGPRs for K = 128.
-    int bv = 32;
+    // fp32 state: 64 columns (two 128-byte lines per row segment, 128 state
+    // VGPRs at K = 128); bf16 state: 32. Both measured on MI355X (spec verify
+    // 276 vs 300 us with fp32 state, 233 vs 249 us with bf16). Narrower where
+    // V or the instance table asks for it.
+    int bv = c.state_dtype == GDN_DTYPE_BF16 ? 32 : 64;
     while (bv > 8 && (c.head_v_dim % bv != 0 || !gdn::instance_exists(c.head_k_dim, bv))) bv /= 2;
     return bv;
 }
@@ -166,9 +168,10 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
     }
 
     if (rows) {
-        // 8 state rows per lane where that instance exists (measured faster
-        // on MI355X than 16: more, smaller workgroups), unless a block_k or
-        // waves_per_group override asks for the other.
+        // fp32 state: 8 state rows per lane where that instance exists
+        // (measured faster on MI355X than 16: more, smaller workgroups);
+        // bf16 state: 16 (304 vs 340 us at bs=512). A block_k or
+        // waves_per_group override may ask for the other.
         int rpl_max = 0;
         if (c.block_k != 0) {
             for (int r : {16, 8})
@@ -177,7 +180,8 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
                 return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
                                                   "wavefront for K = %d, V = %d", c.block_k, K, V);
         } else {
-            for (int r : {8, 16}) {
+            const bool bf16_state = c.state_dtype == GDN_DTYPE_BF16;
+            for (int r : {bf16_state ? 16 : 8, bf16_state ? 8 : 16}) {
                 const int rpw = gdn::rows_per_wave(K, V, r);
                 if (rpw == 0) continue;
                 const int kw = K / rpw;

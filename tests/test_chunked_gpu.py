@@ -208,3 +208,38 @@ def test_chunked_all_padded(dev):
     pool0 = pool.clone()
     out = run_chunked(inp, pool, dev)
     assert torch.isnan(out).all() and torch.equal(pool, pool0)
+
+
+@pytest.mark.parametrize("layout", ["KV", "VK"])
+def test_chunked_strided_and_packed_inputs(dev, layout):
+    """q/k/v as column slices of one fused projection and a/b packed per
+    k-head ([N, H_k, 2G]: the G b-values, then the G a-values) give the dense
+    chunked result bit for bit."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce(f"chunked strided/packed {layout}")
+    wl = W.Workload("ck_strided", 97, 3, 100, 2, 6, 128, 64, W.ACT_BF16, 5, 0.05)
+    inp = W.make_host_inputs(wl)
+    d = W.to_torch(inp, dev)
+    pool_np = to_layout(W.make_pool_host(wl), layout)
+    p_dense = torch.from_numpy(pool_np).to(dev)
+    o_dense = run_chunked(inp, p_dense, dev, layout=layout)
+    N, Hk, Hv, K, V, G = inp.num_tokens, 2, 6, 128, 64, 3
+    width = 2 * Hk * K + Hv * V + 40           # the stride stays a multiple of 8
+    fused = torch.zeros(N, width, dtype=torch.bfloat16, device=dev)
+    fused[:, :Hk * K] = d["q"].reshape(N, -1)
+    fused[:, Hk * K:2 * Hk * K] = d["k"].reshape(N, -1)
+    fused[:, 2 * Hk * K:2 * Hk * K + Hv * V] = d["v"].reshape(N, -1)
+    q = fused[:, :Hk * K].view(N, Hk, K)
+    k = fused[:, Hk * K:2 * Hk * K].view(N, Hk, K)
+    v = fused[:, 2 * Hk * K:2 * Hk * K + Hv * V].view(N, Hv, V)
+    mixed = torch.empty(N, Hk, 2 * G, dtype=torch.bfloat16, device=dev)
+    mixed[:, :, :G] = d["b"].view(N, Hk, G)
+    mixed[:, :, G:] = d["a"].view(N, Hk, G)
+    p_str = torch.from_numpy(pool_np).to(dev)
+    out = torch.full_like(o_dense, float("nan"))
+    gdn.gdn_chunk_gated_delta_rule_fwd(q, k, v, mixed[:, :, G:], mixed[:, :, :G], d["A_log"],
+                                       d["dt_bias"], p_str, d["state_idx"], None, out,
+                                       tokens_per_seq=wl.tokens_per_seq, state_layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_dense) and torch.equal(p_str, p_dense)
