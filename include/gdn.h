@@ -129,7 +129,8 @@ typedef struct gdn_config {
                                 wavefront (dividing V).  A non-zero value with
                                 GDN_KERNEL_AUTO selects the column tiles        */
     int32_t block_k;         /* row split: K-rows per wavefront (rows per lane
-                                16 or 8 times the rows one instruction covers) */
+                                32, 16 or 8 times the rows one instruction
+                                covers)                                        */
     int32_t waves_per_group; /* wavefronts per workgroup, 1..8: column tiles:
                                 dividing G*V/block_v; row split: a multiple of
                                 K/block_k covering a divisor of G heads        */

@@ -168,20 +168,30 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
     }
 
     if (rows) {
-        // fp32 state: 8 state rows per lane where that instance exists
-        // (measured faster on MI355X than 16: more, smaller workgroups);
-        // bf16 state: 16 (304 vs 340 us at bs=512). A block_k or
-        // waves_per_group override may ask for the other.
+        // Rows per lane, from same-box A/B runs on MI355X:
+        //   * fp32 state, K = V = 128 and at least 2048 (sequence, k-head)
+        //     workgroups: 32 (two wavefronts per head; bs=512 351 vs 361 us
+        //     with 8, the TP4 shard 99.1 vs 100.4 us);
+        //   * fp32 state otherwise: 8 (bs=64 51.2 vs 52.0 us with 32);
+        //   * bf16 state: 16 (bs=512 279 vs 320 us with 8).
+        // A block_k or waves_per_group override may ask for another.
         int rpl_max = 0;
         if (c.block_k != 0) {
-            for (int r : {16, 8})
+            for (int r : {16, 8, 32})
                 if (gdn::rows_per_wave(K, V, r) == c.block_k) { rpl_max = r; break; }
             if (!rpl_max)
                 return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
                                                   "wavefront for K = %d, V = %d", c.block_k, K, V);
         } else {
-            const bool bf16_state = c.state_dtype == GDN_DTYPE_BF16;
-            for (int r : {bf16_state ? 16 : 8, bf16_state ? 8 : 16}) {
+            const bool big_grid = K == 128 && V == 128 &&
+                                  static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 2048;
+            int order[3] = {8, 16, 32};
+            if (c.state_dtype == GDN_DTYPE_BF16) {
+                order[0] = 16; order[1] = 8; order[2] = 32;
+            } else if (big_grid) {
+                order[0] = 32; order[1] = 8; order[2] = 16;
+            }
+            for (int r : order) {
                 const int rpw = gdn::rows_per_wave(K, V, r);
                 if (rpw == 0) continue;
                 const int kw = K / rpw;

@@ -26,11 +26,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN); on gfx950
+// the conversion is v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two values rounded to bf16 and packed (the first in the low half): one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16_rne_pair(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) { return bf16_rne(f); }
@@ -93,8 +100,8 @@ __device__ __forceinline__ void store4_act(void* base, int64_t e, float4 o) {
         *reinterpret_cast<float4*>(static_cast<float*>(base) + e) = o;
     } else {
         uint2 w;
-        w.x = bf16_rne(o.x) | (bf16_rne(o.y) << 16);
-        w.y = bf16_rne(o.z) | (bf16_rne(o.w) << 16);
+        w.x = bf16_rne_pair(o.x, o.y);
+        w.y = bf16_rne_pair(o.z, o.w);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + e) = w;
     }
 }

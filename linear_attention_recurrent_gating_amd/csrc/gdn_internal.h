@@ -56,7 +56,7 @@ struct LaunchShape {
     int act;          // 0 = fp32, 1 = bf16
     int multi_token;  // 0: one token per sequence; 1: chunked token loop
     int waves;        // wavefronts per workgroup
-    int rows_rpl_max; // row-split kernel: at most 16 or 8 state rows per lane
+    int rows_rpl_max; // row-split kernel: at most 32, 16 or 8 state rows per lane
     int chunk;        // tokens staged per chunk (1 for the single-token kernel)
     int64_t groups;   // grid size
     int lds_bytes;
@@ -72,7 +72,7 @@ int lds_bytes_for(const LaunchShape& shape, int V);
 bool instance_exists(int K, int block_v);
 
 // Rows per wavefront of the row-split kernel for (K, V) with at most rpl_max
-// (16 or 8) rows per lane; 0 if there is no such instance.
+// (32, 16 or 8) rows per lane; 0 if there is no such instance.
 int rows_per_wave(int K, int V, int rpl_max);
 
 // Value-rows per wavefront of the VK-layout kernel for (K, V); 0 if there is

@@ -87,8 +87,7 @@ __device__ __forceinline__ float4 tile_load(const TileIO& t, uint32_t off) {
 
 __device__ __forceinline__ void tile_store(const TileIO& t, uint32_t off, const float4& s) {
     if (t.bf16) {
-        const u32x2 v = {bf16_rne_bits(s.x) | (bf16_rne_bits(s.y) << 16),
-                         bf16_rne_bits(s.z) | (bf16_rne_bits(s.w) << 16)};
+        const u32x2 v = {bf16_rne_pair(s.x, s.y), bf16_rne_pair(s.z, s.w)};
         __builtin_amdgcn_raw_buffer_store_b64(v, t.r, t.lane_bytes, off << 1, kBufNonTemporal);
         return;
     }
@@ -842,8 +841,8 @@ KernelFn select_columns(int K, int BV, int act, int multi_token) {
     return multi_token ? by_k<1, kChunkTokens>(K, BV) : by_k<1, 1>(K, BV);
 }
 
-// Row-split instances: RPL_MAX 16 (64 state VGPRs per lane) and 8 (32),
-// while a head needs at most 8 wavefronts.
+// Row-split instances: RPL_MAX 32 (128 state VGPRs per lane), 16 (64) and
+// 8 (32), while a head needs at most 8 wavefronts.
 template <int K, int V, int ACT, int RPLM>
 KernelFn pick_rows() {
     if constexpr (RowSplit<K, V, RPLM>::KW <= 8) return &gdn_decode_rows<K, V, ACT, RPLM>;
@@ -852,7 +851,10 @@ KernelFn pick_rows() {
 
 template <int K, int V, int ACT>
 KernelFn rows_by_rpl(int rpl) {
-    return rpl == 8 ? pick_rows<K, V, ACT, 8>() : rpl == 16 ? pick_rows<K, V, ACT, 16>() : nullptr;
+    return rpl == 8    ? pick_rows<K, V, ACT, 8>()
+           : rpl == 16 ? pick_rows<K, V, ACT, 16>()
+           : rpl == 32 ? pick_rows<K, V, ACT, 32>()
+                       : nullptr;
 }
 
 template <int K, int ACT>

@@ -160,10 +160,14 @@ def test_plan_tile_table():
     assert decode.multi_token == 0 and decode.tokens_per_chunk == 1
     assert decode.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     assert decode.block_v == 128                   # whole rows per wavefront
-    assert decode.block_k == 16                    # 8 rows per lane: 8 waves per head
-    assert decode.waves_per_group == 8 and decode.threads_per_group == 512
-    assert decode.workgroups == 512 * 32          # one per (sequence, v-head)
-    assert decode.lds_bytes == (2 * 128 + 8 * (2 * 128 + 4)) * 4
+    assert decode.block_k == 64                    # 32 rows per lane: 2 waves per head
+    assert decode.waves_per_group == 4 and decode.threads_per_group == 256
+    assert decode.workgroups == 512 * 16          # one per (sequence, k-head)
+    assert decode.lds_bytes == (2 * 128 + 4 * (2 * 128 + 4)) * 4
+    # fewer than 2048 (sequence, k-head) pairs: 8 rows per lane, one head per group
+    small = gdn.gdn_plan(base_cfg(num_seqs=64, num_tokens=64, num_k_heads=16, num_v_heads=32,
+                                  num_slots=1024), False)
+    assert small.block_k == 16 and small.waves_per_group == 8 and small.workgroups == 64 * 32
     # K = V = 256 would need 16 row blocks per head: the column-tile kernel takes it
     big = gdn.gdn_plan(base_cfg(head_k_dim=256, head_v_dim=256), False)
     assert big.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and big.block_v == 32

@@ -118,6 +118,22 @@ def test_row_split_eight_rows_per_lane(dev, K, V):
         full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, waves=kw)
 
 
+@pytest.mark.parametrize("K,V", [(32, 32), (64, 64), (128, 32), (128, 64), (128, 128),
+                                 (256, 64), (256, 128)], ids=lambda x: str(x))
+def test_row_split_thirty_two_rows_per_lane(dev, K, V):
+    """Row split with 32 state rows per lane (block_k = 32 * rows per
+    instruction): the instance chosen for large fp32 grids at K = V = 128."""
+    import linear_attention_recurrent_gating_amd as gdn
+    rg = 64 // (V // 4)
+    bk = 32 * rg
+    if bk > K or K // bk > 8:
+        pytest.skip(f"no 32-rows-per-lane instance for K={K}, V={V}")
+    for act, seed in ((W.ACT_BF16, 65), (W.ACT_F32, 66)):
+        wl = W.Workload(f"rows32_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
+                        num_padded=1)
+        full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=bk)
+
+
 def test_decode_kernel_families_agree(dev):
     """The row-split and column-tile single-token kernels differ only in the
     order of their fp32 reductions."""
