@@ -31,11 +31,11 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
 int default_block_v(const gdn_config& c) {
-    // fp32 state: 64 columns (two 128-byte lines per row segment, 128 state
-    // VGPRs at K = 128); bf16 state: 32. Both measured on MI355X (spec verify
-    // 276 vs 300 us with fp32 state, 233 vs 249 us with bf16). Narrower where
-    // V or the instance table asks for it.
-    int bv = c.state_dtype == GDN_DTYPE_BF16 ? 32 : 64;
+    // 64 columns (a 256-byte fp32 or 128-byte bf16 row segment, 128 state
+    // VGPRs at K = 128), measured on MI355X against 32: spec verify 276 vs
+    // 300 us with fp32 state, 202 vs 237 us with bf16. Narrower where V or the
+    // instance table asks for it.
+    int bv = 64;
     while (bv > 8 && (c.head_v_dim % bv != 0 || !gdn::instance_exists(c.head_k_dim, bv))) bv /= 2;
     return bv;
 }
@@ -169,11 +169,13 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
 
     if (rows) {
         // Rows per lane, from same-box A/B runs on MI355X:
+        //   * bf16 state at K = V = 128: 32 (bs=512 187 vs 201 us with 16,
+        //     bs=64 31.0 vs 32.1 us);
         //   * fp32 state, K = V = 128 and at least 2048 (sequence, k-head)
         //     workgroups: 32 (two wavefronts per head; bs=512 351 vs 361 us
         //     with 8, the TP4 shard 99.1 vs 100.4 us);
-        //   * fp32 state otherwise: 8 (bs=64 51.2 vs 52.0 us with 32);
-        //   * bf16 state: 16 (bs=512 279 vs 320 us with 8).
+        //   * otherwise 8 for fp32 state (bs=64 51.2 vs 52.0 us with 32) and
+        //     16 for bf16.
         // A block_k or waves_per_group override may ask for another.
         int rpl_max = 0;
         if (c.block_k != 0) {
@@ -183,13 +185,14 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
                 return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
                                                   "wavefront for K = %d, V = %d", c.block_k, K, V);
         } else {
-            const bool big_grid = K == 128 && V == 128 &&
-                                  static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 2048;
+            const bool kv128 = K == 128 && V == 128;
+            const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
+            const bool big_grid = static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 2048;
             int order[3] = {8, 16, 32};
-            if (c.state_dtype == GDN_DTYPE_BF16) {
+            if (kv128 && (bf16 || big_grid)) {
+                order[0] = 32; order[1] = bf16 ? 16 : 8; order[2] = bf16 ? 8 : 16;
+            } else if (bf16) {
                 order[0] = 16; order[1] = 8; order[2] = 32;
-            } else if (big_grid) {
-                order[0] = 32; order[1] = 8; order[2] = 16;
             }
             for (int r : order) {
                 const int rpw = gdn::rows_per_wave(K, V, r);

@@ -171,6 +171,14 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
     return x;
 }
 
+// Returns x unchanged but hidden from the optimiser, so that values derived
+// from it (per-row buffer offsets) are formed where they are used instead of
+// being hoisted out of a loop and kept live in scalar registers across it.
+__device__ __forceinline__ uint32_t opaque_uniform(uint32_t x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // Workgroup barrier that orders LDS only: global loads already in flight (the
 // state tile) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

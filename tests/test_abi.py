@@ -178,12 +178,12 @@ def test_plan_tile_table():
     assert spec.waves_per_group == 4             # G * V / 64 = 4 tile units per k-head
     spec16 = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
                                    num_slots=1024, state_dtype=gdn.GDN_DTYPE_BF16), True)
-    assert spec16.block_v == 32                   # bf16 state: 32 columns
+    assert spec16.block_v == 64 and spec16.waves_per_group == 4   # bf16 state: 64 columns too
     multi = gdn.gdn_plan(base_cfg(tokens_per_seq=4, num_tokens=16), False)
     assert multi.multi_token == 1
     # bf16 state: 16 rows per lane in the row split
     dec16 = gdn.gdn_plan(base_cfg(state_dtype=gdn.GDN_DTYPE_BF16), False)
-    assert dec16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and dec16.block_k == 32
+    assert dec16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and dec16.block_k == 64   # 32 rows per lane
     # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
     odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32), True)
     assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
