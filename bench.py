@@ -37,9 +37,18 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 KERNEL_NAMES = {1: "gdn_fused_update", 2: "gdn_decode_rows", 3: "gdn_vk_update",
                 4: "gdn_chunk_fwd"}  # by kernel_family
+ROW_SPLIT_TOKEN_LOOP = "gdn_rows_tokens"  # family 2 over several tokens per sequence
 # The sources each kernel is compiled from (the counter profiles are keyed to them).
-KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_device.h", "gdn_internal.h")}
-DEFAULT_SOURCES = ("gdn_kernels.hip", "gdn_device.h", "gdn_internal.h")
+_ROWS = ("gdn_rows.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
+KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_device.h", "gdn_internal.h"),
+                  "gdn_decode_rows": _ROWS, ROW_SPLIT_TOKEN_LOOP: _ROWS}
+DEFAULT_SOURCES = ("gdn_kernels.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
+
+
+def kernel_name(info) -> str:
+    if info.kernel_family == 2 and info.multi_token:
+        return ROW_SPLIT_TOKEN_LOOP
+    return KERNEL_NAMES[info.kernel_family]
 
 
 def kernel_source_hash(kernel: str = "gdn_decode_rows") -> str:
@@ -341,7 +350,7 @@ def main():
                    "head_k_dim": wl.head_k_dim, "head_v_dim": wl.head_v_dim,
                    "activations": wl.act, "state": args.state_dtype, "state_layout": args.layout,
                    "pool_slots": wl.num_slots,
-                   "slot_sets": sets, "kernel": KERNEL_NAMES[info.kernel_family],
+                   "slot_sets": sets, "kernel": kernel_name(info),
                    "block_v": info.block_v, "block_k": info.block_k,
                    "waves_per_group": info.waves_per_group, "workgroups": info.workgroups,
                    "gates": "unfused pair (gdn_gating + gdn_recurrent_update)" if args.unfused
@@ -352,8 +361,8 @@ def main():
         "kernel_us": kern_ms * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(KERNEL_NAMES[info.kernel_family], wl.name),
-                     "algorithmic_bytes": alg_bytes, "kernel": KERNEL_NAMES[info.kernel_family]},
+                     "traffic": counter_traffic(kernel_name(info), wl.name),
+                     "algorithmic_bytes": alg_bytes, "kernel": kernel_name(info)},
         "cpu_baseline": None,
     }
     if info.kernel_family == gdn.GDN_KERNEL_CHUNKED:

@@ -122,9 +122,10 @@ typedef struct gdn_config {
     int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): the chunked kernel for
                                 calls without intermediate states averaging at
                                 least 32 tokens per sequence (K, V <= 128);
-                                otherwise, with GDN_LAYOUT_KV, row split for
-                                one token per sequence and column tiles for
-                                more; with GDN_LAYOUT_VK, value rows           */
+                                otherwise, with GDN_LAYOUT_KV, row split
+                                (column tiles where no row-split instance
+                                fits, or block_v is set); with GDN_LAYOUT_VK,
+                                value rows                                     */
     int32_t block_v;         /* column tiles: 8, 16, 32 or 64 V-columns per
                                 wavefront (dividing V).  A non-zero value with
                                 GDN_KERNEL_AUTO selects the column tiles        */
@@ -141,7 +142,7 @@ typedef struct gdn_config {
 #define GDN_KERNEL_COLUMN_TILES 1 /* wavefront = (v-head, block_v columns, all K
                                      rows); any number of tokens               */
 #define GDN_KERNEL_ROW_SPLIT 2    /* wavefront = (v-head, all V columns, block_k
-                                     rows); one token per sequence             */
+                                     rows); any number of tokens               */
 #define GDN_KERNEL_VALUE_ROWS 3   /* GDN_LAYOUT_VK only: wavefront = (v-head,
                                      block of whole value-rows); any number of
                                      tokens                                    */

@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -14,7 +15,7 @@ LIB = os.path.join(LIBDIR, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_INCLUDE = "/opt/rocm/include"
 
-DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_chunk.hip"]
+DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_rows.hip", "gdn_chunk.hip"]
 HOST_SOURCES = ["gdn_api.cpp"]
 
 # Packed fp32 VALU forms are disabled: hipcc -O3 otherwise forms them from
@@ -33,18 +34,21 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, extra_device_flags=()) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in DEVICE_SOURCES:
         obj = os.path.join(LIBDIR, src + ".o")
-        _run([HIPCC, *COMMON, *DEVICE, *extra_device_flags, "-c", os.path.join(CSRC, src), "-o", obj],
-             verbose)
+        cmds.append([HIPCC, *COMMON, *DEVICE, *extra_device_flags, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(LIBDIR, src + ".o")
-        _run([HIPCC, *COMMON, "-I", ROCM_INCLUDE, "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
-              os.path.join(CSRC, src),
-              "-o", obj], verbose)
+        cmds.append([HIPCC, *COMMON, "-I", ROCM_INCLUDE, "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # one compiler process per source, at most MAX_JOBS (default 4) at a time
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "4"))))
+    with ThreadPoolExecutor(jobs) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

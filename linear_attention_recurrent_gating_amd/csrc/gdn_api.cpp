@@ -40,6 +40,9 @@ int default_block_v(const gdn_config& c) {
     return bv;
 }
 
+// Dynamic LDS a per-token kernel may ask for (the default launch limit).
+constexpr int kMaxDynamicLds = 64 * 1024;
+
 // Largest divisor of `units` (wave units per k-head) not above 8.
 int default_waves(int units) {
     for (int w = 8; w >= 1; --w)
@@ -99,10 +102,12 @@ bool auto_chunked(const gdn_config& c, bool has_inter) {
 }
 
 // Chooses the kernel family, tile and grid of a (size-checked) config, and
-// rejects tiling overrides that have no kernel instance.  Single-token calls
-// default to the row-split kernel (one contiguous kilobyte per load/store
-// instruction); multi-token calls, and calls that override block_v, use the
-// column-tile kernel.
+// rejects tiling overrides that have no kernel instance.  Calls that the
+// chunked kernel does not take default to the row-split kernel (one
+// contiguous kilobyte per load/store instruction; measured on MI355X against
+// the column tiles: spec verify 264 vs 282 us, the long-varlen batch per
+// token 1.67 vs 2.45 ms); calls that override block_v, and shapes without a
+// row-split instance, use the column-tile kernel.
 gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::LaunchShape& s) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
@@ -154,9 +159,6 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
 
     bool rows;
     if (c.kernel_family == GDN_KERNEL_ROW_SPLIT) {
-        if (s.multi_token)
-            return fail(GDN_ERR_BAD_ARGUMENT,
-                        "the row-split kernel handles one token per sequence (no cu_seqlens, T = 1)");
         if (c.block_v != 0 && c.block_v != V)
             return fail(GDN_ERR_BAD_ARGUMENT, "the row-split kernel covers all V columns "
                                               "(block_v must be 0 or V = %d)", V);
@@ -164,18 +166,19 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
     } else if (c.kernel_family == GDN_KERNEL_COLUMN_TILES) {
         rows = false;
     } else {
-        rows = !s.multi_token && c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0;
+        rows = c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0;
     }
 
     if (rows) {
         // Rows per lane, from same-box A/B runs on MI355X:
-        //   * bf16 state at K = V = 128: 32 (bs=512 187 vs 201 us with 16,
-        //     bs=64 31.0 vs 32.1 us);
-        //   * fp32 state, K = V = 128 and at least 2048 (sequence, k-head)
-        //     workgroups: 32 (two wavefronts per head; bs=512 351 vs 361 us
-        //     with 8, the TP4 shard 99.1 vs 100.4 us);
-        //   * otherwise 8 for fp32 state (bs=64 51.2 vs 52.0 us with 32) and
-        //     16 for bf16.
+        //   * K = V = 128 and at least 2048 (sequence, k-head) workgroups:
+        //     32 (two wavefronts per head; bs=512 decode 351 vs 361 us with 8,
+        //     the TP4 shard 99.1 vs 100.4 us, spec verify 264 vs 300 us);
+        //   * bf16 state, one token, K = V = 128: 32 as well (bs=64 31.0 vs
+        //     32.1 us with 16);
+        //   * otherwise 8 for fp32 state and for token loops (bs=64 51.2 vs
+        //     52.0 us with 32; 8 long sequences 1.67 vs 2.70 ms), 16 for a
+        //     single bf16 token.
         // A block_k or waves_per_group override may ask for another.
         int rpl_max = 0;
         if (c.block_k != 0) {
@@ -189,9 +192,9 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
             const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
             const bool big_grid = static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 2048;
             int order[3] = {8, 16, 32};
-            if (kv128 && (bf16 || big_grid)) {
+            if (kv128 && (big_grid || (bf16 && !s.multi_token))) {
                 order[0] = 32; order[1] = bf16 ? 16 : 8; order[2] = bf16 ? 8 : 16;
-            } else if (bf16) {
+            } else if (bf16 && !s.multi_token) {
                 order[0] = 16; order[1] = 8; order[2] = 32;
             }
             for (int r : order) {
@@ -201,15 +204,31 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
                 if (c.waves_per_group != 0 &&
                     (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0))
                     continue;
+                gdn::LaunchShape one = s;   // one head per workgroup must fit the LDS budget
+                one.kind = gdn::kKindRows;
+                one.block_k = rpw;
+                one.waves = kw;
+                if (gdn::lds_bytes_for(one, V) > kMaxDynamicLds) continue;
                 rpl_max = r;
                 break;
             }
-            if (!rpl_max) rpl_max = 16;   // reported below
+            if (!rpl_max)
+                return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel fits K = %d, V = %d (at most 8 "
+                                                  "wavefronts per head, %d bytes of LDS, waves_per_group)",
+                            K, V, kMaxDynamicLds);
         }
         const int rpw = gdn::rows_per_wave(K, V, rpl_max);
         if (rpw == 0)
             return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel for K = %d, V = %d", K, V);
         const int kw = K / rpw;
+        s.kind = gdn::kKindRows;
+        s.block_v = V;
+        s.block_k = rpw;
+        s.rows_rpl_max = rpl_max;
+        const auto lds_for = [&](int hp) {
+            s.waves = hp * kw;
+            return gdn::lds_bytes_for(s, V);
+        };
         int heads = 0;
         if (c.waves_per_group != 0) {
             if (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0)
@@ -217,14 +236,16 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
                             "waves_per_group = %d must be a multiple of the %d wavefronts per head "
                             "covering a divisor of G = %d heads", c.waves_per_group, kw, G);
             heads = c.waves_per_group / kw;
+            if (lds_for(heads) > kMaxDynamicLds)
+                return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d needs %d bytes of LDS (at most "
+                                                  "%d)", c.waves_per_group, lds_for(heads), kMaxDynamicLds);
         } else {
-            for (int hp = G; hp >= 1 && !heads; --hp)  // largest divisor of G within 8 waves
-                if (G % hp == 0 && hp * kw <= 8) heads = hp;
+            // largest divisor of G within 8 waves and the LDS budget
+            for (int hp = G; hp >= 1 && !heads; --hp)
+                if (G % hp == 0 && hp * kw <= 8 && lds_for(hp) <= kMaxDynamicLds) heads = hp;
+            if (!heads)
+                return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no row-split workgroup fits the LDS budget");
         }
-        s.kind = gdn::kKindRows;
-        s.block_v = V;
-        s.block_k = rpw;
-        s.rows_rpl_max = rpl_max;
         s.waves = heads * kw;
         s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (G / heads);
     } else {

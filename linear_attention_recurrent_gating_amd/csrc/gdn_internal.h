@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (gdn_api.cpp) and the
-// device code (gdn_kernels.hip).  Not installed; not part of the ABI.
+// device code (gdn_kernels.hip, gdn_rows.hip, gdn_chunk.hip).  Not installed;
+// not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,6 +71,14 @@ int lds_bytes_for(const LaunchShape& shape, int V);
 
 // True when a column-tile kernel instance exists for (K, block_v).
 bool instance_exists(int K, int block_v);
+
+// A fused-update kernel entry (every instance takes the parameter block by
+// value).
+using KernelFn = void (*)(FusedParams);
+
+// The row-split kernel for (K, V, activation dtype, at most rpl_max rows per
+// lane); multi_token selects the token-loop variant.  nullptr if none.
+KernelFn select_rows(int K, int V, int act, int rpl_max, int multi_token);
 
 // Rows per wavefront of the row-split kernel for (K, V) with at most rpl_max
 // (32, 16 or 8) rows per lane; 0 if there is no such instance.

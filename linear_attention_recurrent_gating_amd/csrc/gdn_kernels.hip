@@ -32,156 +32,10 @@
 // in LDS, computes the gates of the chunk one token per lane, and then runs
 // the dependent token loop with the state resident in VGPRs.
 
-#include "gdn_device.h"
+#include "gdn_tile.h"
 
 namespace gdn {
 namespace {
-
-constexpr int kMaxThreads = 512;
-
-// The state streams through HBM once per call (read, then written back), so
-// its loads and stores carry the non-temporal hint.  They are raw buffer
-// operations on a resource that spans exactly one K x V tile: the tile base
-// sits in SGPRs, each lane keeps one 32-bit byte offset in a VGPR, and the
-// row-group step is a scalar offset -- no 64-bit address per row stays live
-// between the loads and the final stores.  Offsets past the tile would be
-// clamped by the hardware (loads return 0, stores are dropped).  Tiles may be
-// stored as bf16 (64-bit accesses per four elements, rounded to nearest even
-// on the way out); the state is fp32 in registers either way.
-
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// One K x V state tile in the pool or in intermediate_states, stored as fp32
-// or as bf16 (the arithmetic is fp32 either way).  Offsets are in elements;
-// `lane` is this lane's element offset within the tile.
-struct TileIO {
-    __amdgpu_buffer_rsrc_t r;
-    uint32_t lane_bytes;
-    bool bf16;
-};
-
-__device__ __forceinline__ TileIO tile_io(const void* base, bool bf16, size_t tile_index,
-                                          size_t tile_elems, uint32_t lane) {
-    const int sh = bf16 ? 1 : 2;
-    const char* b = static_cast<const char*>(base) + ((tile_index * tile_elems) << sh);
-    TileIO t;
-    t.r = buffer_rsrc(b, static_cast<uint32_t>(tile_elems << sh));
-    t.lane_bytes = lane << sh;
-    t.bf16 = bf16;
-    return t;
-}
-
-// Issues the loads of N groups of four consecutive state elements, group i at
-// element offset off(i) past the lane's, as raw words (fp32: four words; bf16:
-// two words in .x/.y).  One branch on the storage type covers all N loads, so
-// none waits for another; tile_unpack, placed at the first use, waits for them.
-template <int N, typename OFF>
-__device__ __forceinline__ void tile_issue(const TileIO& t, OFF off, u32x4 (&raw)[N]) {
-    if (t.bf16) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(t.r, t.lane_bytes, off(i) << 1,
-                                                                 kBufNonTemporal);
-            raw[i].x = v[0];
-            raw[i].y = v[1];
-        }
-    } else {
-        // 16 idle cycles between the 1 KiB fp32 loads of a wavefront: measured
-        // on MI355X against back-to-back issue, the bs=512 decode takes 352.7
-        // vs 355.5 us and the spec-verify batch 282 vs 286 us (other
-        // wavefronts' accesses interleave instead of queueing behind a burst).
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            raw[i] = __builtin_amdgcn_raw_buffer_load_b128(t.r, t.lane_bytes, off(i) << 2, kBufNonTemporal);
-            asm volatile("s_nop 7\n\ts_nop 7");
-        }
-    }
-}
-
-// Widens raw words from tile_issue to fp32 (bf16 -> fp32 is exact).
-template <int N>
-__device__ __forceinline__ void tile_unpack(bool bf16, const u32x4 (&raw)[N], float4 (&s)[N]) {
-    if (bf16) {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            s[i] = make_float4(__uint_as_float(raw[i].x << 16), __uint_as_float(raw[i].x & 0xffff0000u),
-                               __uint_as_float(raw[i].y << 16), __uint_as_float(raw[i].y & 0xffff0000u));
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            s[i] = make_float4(__uint_as_float(raw[i].x), __uint_as_float(raw[i].y),
-                               __uint_as_float(raw[i].z), __uint_as_float(raw[i].w));
-    }
-}
-
-// Stores N groups of four state elements (group i at element offset off(i)
-// past the lane's), rounding to bf16 (nearest even) for bf16 storage.
-template <int N, typename OFF>
-__device__ __forceinline__ void tile_store_all(const TileIO& t, OFF off, const float4 (&s)[N]) {
-    if (t.bf16) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const u32x2 v = {bf16_rne_pair(s[i].x, s[i].y), bf16_rne_pair(s[i].z, s[i].w)};
-            __builtin_amdgcn_raw_buffer_store_b64(v, t.r, t.lane_bytes, off(i) << 1, kBufNonTemporal);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const u32x4 v = {__float_as_uint(s[i].x), __float_as_uint(s[i].y), __float_as_uint(s[i].z),
-                             __float_as_uint(s[i].w)};
-            __builtin_amdgcn_raw_buffer_store_b128(v, t.r, t.lane_bytes, off(i) << 2, kBufNonTemporal);
-        }
-    }
-}
-
-// ----------------------------------------------------------- q/k staging
-// Normalises q and k of tokens [c0, c0+nt) of k-head j into qs/ks ([nt][K]
-// floats each), element kappa of a token going to position POS(kappa).  Each
-// 16-lane DPP row of the workgroup handles one vector (the q or the k of one
-// token): K/16 elements per lane, a row reduction, one rsqrt.  q carries the
-// query scale.  Every vector is reduced in the same order, whichever row
-// handles it.
-template <int K, int ACT, typename POS>
-__device__ __forceinline__ void stage_qk(const FusedParams& p, float* qs, float* ks, int j,
-                                         int64_t c0, int nt, int wave, int waves, int lane,
-                                         POS pos) {
-    constexpr int EPL = K / 16;
-    const int lr = lane % 16;
-    for (int vec = wave * 4 + lane / 16; vec < 2 * nt; vec += 4 * waves) {
-        const int tok = vec >> 1;
-        const bool is_k = vec & 1;
-        const int64_t t = c0 + tok;
-        float x[EPL];
-        if (is_k)
-            load_act<ACT, EPL>(p.k, t * p.k_stride + static_cast<int64_t>(j) * K + lr * EPL, x);
-        else
-            load_act<ACT, EPL>(p.q, t * p.q_stride + static_cast<int64_t>(j) * K + lr * EPL, x);
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-        ss = sum_dpp_row(ss);
-        const float f = (is_k ? 1.0f : p.scale) * rsqrtf(ss + p.eps);
-        float* dst = (is_k ? ks : qs) + tok * K;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dst[pos(lr * EPL + e)] = x[e] * f;
-    }
-}
-
-// Reads N consecutive LDS floats (16-byte aligned when N % 4 == 0).
-template <int N>
-__device__ __forceinline__ void lds_read(const float* src, float (&x)[N]) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const float4 t = reinterpret_cast<const float4*>(src)[i];
-            x[4 * i] = t.x; x[4 * i + 1] = t.y; x[4 * i + 2] = t.z; x[4 * i + 3] = t.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) x[i] = src[i];
-    }
-}
 
 // ------------------------------------------------------- column-tile kernel
 template <int K, int BV, int ACT, int CHUNK>
@@ -356,191 +210,6 @@ gdn_fused_update(const FusedParams p) {
         stage(c0, nt);
     }
 
-    if (p.write_final) tile_store_all<RPL>(tio, rows_at, S);
-}
-
-
-// ----------------------------------------------------------- row-split kernel
-// Single-token decode with whole rows per wavefront.  LPR = V/4 lanes cover
-// one V-column row, so each 128-bit load or store instruction of a wave moves
-// RG = 64/LPR consecutive rows: one contiguous kilobyte of the tile.  Lane l
-// holds columns 4*(l % LPR)..+3 of rows kw*RPW + RG*i + l/LPR (i < RPL); the
-// K rows of a head are split over KW wavefronts.  S^T k, S^T q and k.q are
-// reduced in-lane, across the wave's row groups with permlane swaps, and
-// across the KW wavefronts of the head through LDS, summed in a fixed order
-// so every wave derives the same u.
-template <int K, int V, int RPL_MAX>
-struct RowSplit {
-    static constexpr int LPR = V / 4;                                   // lanes per row
-    static constexpr int RG = kWave / LPR;                              // rows per instruction
-    static constexpr int RPL = (K / RG < RPL_MAX) ? K / RG : RPL_MAX;   // rows per lane
-    static constexpr int RPW = RPL * RG;                                // rows per wave
-    static constexpr int KW = K / RPW;                                  // waves per head
-    static constexpr int PART = 2 * V + 4;                              // partial sums per wave
-};
-
-// The single token's q and k for the row-split kernel, in two halves so the
-// raw loads can be issued ahead of the state loads: DPP rows 0 and 1 of
-// wavefront 0 hold q and k, K/16 elements per lane.
-template <int K, int ACT>
-struct SingleTokenQK {
-    static constexpr int EPL = K / 16;
-    float x[EPL];
-    bool active, is_k;
-
-    __device__ __forceinline__ void load(const FusedParams& p, int j, int64_t t, int wave,
-                                         int lane) {
-        const int vec = wave * 4 + lane / 16;
-        active = vec < 2;
-        is_k = vec == 1;
-        if (active) {
-            const int lr = lane % 16;
-            if (is_k)
-                load_act<ACT, EPL>(p.k, t * p.k_stride + static_cast<int64_t>(j) * K + lr * EPL, x);
-            else
-                load_act<ACT, EPL>(p.q, t * p.q_stride + static_cast<int64_t>(j) * K + lr * EPL, x);
-        }
-    }
-
-    // Same arithmetic, in the same order, as stage_qk.
-    template <typename POS>
-    __device__ __forceinline__ void finish(const FusedParams& p, float* qs, float* ks, int lane,
-                                           POS pos) {
-        if (!active) return;
-        const int lr = lane % 16;
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-        ss = sum_dpp_row(ss);
-        const float f = (is_k ? 1.0f : p.scale) * rsqrtf(ss + p.eps);
-        float* dst = is_k ? ks : qs;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) dst[pos(lr * EPL + e)] = x[e] * f;
-    }
-};
-
-template <int K, int V, int ACT, int RPL_MAX>
-__global__ void __launch_bounds__(kMaxThreads)
-gdn_decode_rows(const FusedParams p) {
-    using L = RowSplit<K, V, RPL_MAX>;
-    constexpr int LPR = L::LPR, RG = L::RG, RPL = L::RPL, RPW = L::RPW, KW = L::KW;
-    static_assert(LPR >= 8 && RPL >= 1 && K % RPW == 0, "unsupported K/V pair");
-
-    extern __shared__ __align__(16) float lds[];
-    float* qs = lds;              // [K] normalised q, permuted
-    float* ks = lds + K;          // [K] normalised k, permuted
-    float* part = lds + 2 * K;    // [heads in group][KW][PART] partial sums
-
-    const int waves = blockDim.x / kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = threadIdx.x % kWave;
-
-    int64_t blk = blockIdx.x;
-    const int gslice = static_cast<int>(blk % p.groups_per_khead);
-    blk /= p.groups_per_khead;
-    const int j = static_cast<int>(blk % p.Hk);
-    const int seq = static_cast<int>(blk / p.Hk);
-
-    const int32_t slot = p.state_idx[seq];
-    if (slot < 0) return;                         // padded: touch nothing
-    const int64_t t = static_cast<int64_t>(seq);  // one token per sequence
-
-    const int heads_per_group = waves / KW;
-    const int hl = wave / KW;                     // head within the workgroup
-    const int kw = wave % KW;                     // row block of the head
-    const int h = j * p.G + gslice * heads_per_group + hl;
-    const int col = 4 * (lane % LPR);
-    const int rg = lane / LPR;
-
-    // Small loads first (q/k for the staging rows, gates, v): they return
-    // while the state tile is still streaming in.
-    SingleTokenQK<K, ACT> qk;
-    qk.load(p, j, t, wave, lane);
-    float gamma, beta;
-    token_gates<ACT>(p, t, h, gamma, beta);
-    float vv[4];
-    load_act<ACT, 4>(p.v, t * p.v_stride + static_cast<int64_t>(h) * V + col, vv);
-
-    constexpr uint32_t row_step = RG * V;   // one kilobyte of fp32 state
-    const uint32_t lane_elem = static_cast<uint32_t>((kw * RPW + rg) * V + col);
-    const TileIO tio = tile_io(p.pool, p.state_bf16, static_cast<size_t>(slot) * p.Hv + h, K * V, lane_elem);
-
-    const auto rows_at = [](int i) { return static_cast<uint32_t>(i) * row_step; };
-    u32x4 raw[RPL];
-    tile_issue<RPL>(tio, rows_at, raw);
-
-    // rows kw*RPW + RG*i + rg of the head sit at kw*RPW + rg*RPL + i
-    qk.finish(p, qs, ks, lane, [](int kappa) {
-        const int r = kappa % RPW;
-        return (kappa - r) + (r % RG) * RPL + r / RG;
-    });
-    lds_barrier();
-
-    float kh[RPL], qh[RPL];
-    lds_read<RPL>(ks + kw * RPW + rg * RPL, kh);
-    lds_read<RPL>(qs + kw * RPW + rg * RPL, qh);
-    float4 S[RPL];
-    tile_unpack<RPL>(tio.bf16, raw, S);
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const float s4[4] = {S[i].x, S[i].y, S[i].z, S[i].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            pk[c] = __builtin_fmaf(s4[c], kh[i], pk[c]);
-            pq[c] = __builtin_fmaf(s4[c], qh[i], pq[c]);
-        }
-        kq = __builtin_fmaf(kh[i], qh[i], kq);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        pk[c] = sum_row_groups<LPR>(pk[c]);
-        pq[c] = sum_row_groups<LPR>(pq[c]);
-    }
-    kq = sum_row_groups<LPR>(kq);
-
-    float* mine = part + (hl * KW + kw) * L::PART;
-    if (rg == 0) {
-        *reinterpret_cast<float4*>(mine + col) = make_float4(pk[0], pk[1], pk[2], pk[3]);
-        *reinterpret_cast<float4*>(mine + V + col) = make_float4(pq[0], pq[1], pq[2], pq[3]);
-        if (lane == 0) mine[2 * V] = kq;
-    }
-    lds_barrier();
-
-    float4 PK = make_float4(0.f, 0.f, 0.f, 0.f), PQ = PK;
-    float KQ = 0.f;
-    const float* head_part = part + hl * KW * L::PART;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) {
-        const float4 a4 = *reinterpret_cast<const float4*>(head_part + w * L::PART + col);
-        const float4 b4 = *reinterpret_cast<const float4*>(head_part + w * L::PART + V + col);
-        PK.x += a4.x; PK.y += a4.y; PK.z += a4.z; PK.w += a4.w;
-        PQ.x += b4.x; PQ.y += b4.y; PQ.z += b4.z; PQ.w += b4.w;
-        KQ += head_part[w * L::PART + 2 * V];
-    }
-
-    float4 u, o;
-    u.x = beta * (vv[0] - gamma * PK.x);
-    u.y = beta * (vv[1] - gamma * PK.y);
-    u.z = beta * (vv[2] - gamma * PK.z);
-    u.w = beta * (vv[3] - gamma * PK.w);
-    o.x = __builtin_fmaf(u.x, KQ, gamma * PQ.x);
-    o.y = __builtin_fmaf(u.y, KQ, gamma * PQ.y);
-    o.z = __builtin_fmaf(u.z, KQ, gamma * PQ.z);
-    o.w = __builtin_fmaf(u.w, KQ, gamma * PQ.w);
-    if (kw == 0 && rg == 0) store4_act<ACT>(p.out, (t * p.Hv + h) * static_cast<int64_t>(V) + col, o);
-
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        S[i].x = __builtin_fmaf(kh[i], u.x, gamma * S[i].x);
-        S[i].y = __builtin_fmaf(kh[i], u.y, gamma * S[i].y);
-        S[i].z = __builtin_fmaf(kh[i], u.z, gamma * S[i].z);
-        S[i].w = __builtin_fmaf(kh[i], u.w, gamma * S[i].w);
-    }
-    if (p.inter) {
-        const TileIO it = tile_io(p.inter, p.state_bf16, static_cast<size_t>(t) * p.Hv + h, K * V, lane_elem);
-        tile_store_all<RPL>(it, rows_at, S);
-    }
     if (p.write_final) tile_store_all<RPL>(tio, rows_at, S);
 }
 
@@ -850,7 +519,6 @@ gdn_gating_kernel(const void* a, const void* b, const float* A_log, const float*
 }
 
 // ------------------------------------------------------------ instance table
-using KernelFn = void (*)(FusedParams);
 
 // A (K, BV) pair has an instance when the K x BV fp32 tile fits in at most
 // 128 VGPRs per lane.
@@ -888,49 +556,6 @@ KernelFn select_columns(int K, int BV, int act, int multi_token) {
     if (act == 0) return multi_token ? by_k<0, kChunkTokens>(K, BV) : by_k<0, 1>(K, BV);
     return multi_token ? by_k<1, kChunkTokens>(K, BV) : by_k<1, 1>(K, BV);
 }
-
-// Row-split instances: RPL_MAX 32 (128 state VGPRs per lane), 16 (64) and
-// 8 (32), while a head needs at most 8 wavefronts.
-template <int K, int V, int ACT, int RPLM>
-KernelFn pick_rows() {
-    if constexpr (RowSplit<K, V, RPLM>::KW <= 8) return &gdn_decode_rows<K, V, ACT, RPLM>;
-    else return nullptr;
-}
-
-template <int K, int V, int ACT>
-KernelFn rows_by_rpl(int rpl) {
-    return rpl == 8    ? pick_rows<K, V, ACT, 8>()
-           : rpl == 16 ? pick_rows<K, V, ACT, 16>()
-           : rpl == 32 ? pick_rows<K, V, ACT, 32>()
-                       : nullptr;
-}
-
-template <int K, int ACT>
-KernelFn rows_by_v(int V, int rpl) {
-    switch (V) {
-        case 32: return rows_by_rpl<K, 32, ACT>(rpl);
-        case 64: return rows_by_rpl<K, 64, ACT>(rpl);
-        case 128: return rows_by_rpl<K, 128, ACT>(rpl);
-        case 256: return rows_by_rpl<K, 256, ACT>(rpl);
-        default: return nullptr;
-    }
-}
-
-template <int ACT>
-KernelFn rows_by_k(int K, int V, int rpl) {
-    switch (K) {
-        case 32: return rows_by_v<32, ACT>(V, rpl);
-        case 64: return rows_by_v<64, ACT>(V, rpl);
-        case 128: return rows_by_v<128, ACT>(V, rpl);
-        case 256: return rows_by_v<256, ACT>(V, rpl);
-        default: return nullptr;
-    }
-}
-
-KernelFn select_rows(int K, int V, int act, int rpl) {
-    return act == 0 ? rows_by_k<0>(K, V, rpl) : rows_by_k<1>(K, V, rpl);
-}
-
 template <int K, int V, int ACT>
 KernelFn pick_vk(int multi) {
     return multi ? &gdn_vk_multi<K, V, ACT, kChunkTokens> : &gdn_vk_decode<K, V, ACT>;
@@ -988,18 +613,17 @@ bool instance_exists(int K, int block_v) {
     return select_columns(K, block_v, 0, 0) != nullptr;
 }
 
-int rows_per_wave(int K, int V, int rpl_max) {
-    if (!select_rows(K, V, 0, rpl_max)) return 0;
-    const int rg = kWave / (V / 4);
-    const int rpl = K / rg < rpl_max ? K / rg : rpl_max;
-    return rpl * rg;
-}
-
 int lds_bytes_for(const LaunchShape& s, int V) {
     int floats = 2 * s.chunk * s.K;                          // normalised q and k
     if (s.kind == kKindColumns && s.multi_token)
         floats += s.waves * s.chunk * s.block_v;             // per-wave v rows
-    if (s.kind == kKindRows) floats += s.waves * (2 * V + 4);  // per-wave partial sums
+    if (s.kind == kKindRows) {
+        const int heads = s.waves / (s.K / s.block_k);
+        if (s.multi_token)  // staged v rows per head, partial sums double-buffered
+            floats += heads * s.chunk * V + 2 * s.waves * (2 * V + 4);
+        else
+            floats += s.waves * (2 * V + 4);                  // per-wave partial sums
+    }
     if (s.kind == kKindValueRows)                             // single token: no LDS at all
         floats = s.multi_token ? 2 * s.chunk * s.K + s.waves * s.chunk * s.block_v : 0;
     return floats * static_cast<int>(sizeof(float));
@@ -1018,7 +642,7 @@ hipError_t launch_gating(const void* a, const void* b, const float* A_log, const
 }
 
 hipError_t launch_fused(const LaunchShape& s, const FusedParams& p, hipStream_t stream) {
-    KernelFn fn = s.kind == kKindRows        ? select_rows(s.K, p.V, s.act, s.rows_rpl_max)
+    KernelFn fn = s.kind == kKindRows        ? select_rows(s.K, p.V, s.act, s.rows_rpl_max, s.multi_token)
                   : s.kind == kKindValueRows ? select_vk(s.K, p.V, s.act, s.multi_token)
                                              : select_columns(s.K, s.block_v, s.act, s.multi_token);
     if (!fn) return hipErrorInvalidDeviceFunction;

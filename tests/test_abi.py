@@ -113,9 +113,9 @@ def test_unsupported_block_for_k():
     assert validate(base_cfg(head_k_dim=256, block_v=64)) == 7
     # column tiles: waves must divide G*V/block_v = 8
     assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES, waves_per_group=3)) == 7
-    # the row-split kernel takes one token per sequence
+    # the row-split kernel takes any number of tokens per sequence
     assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT, tokens_per_seq=2,
-                             num_tokens=8)) == 7
+                             num_tokens=8)) == 0
     assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT, block_v=32)) == 7
     # column tiles cover all K rows
     assert validate(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES, block_k=32)) == 7
@@ -174,18 +174,24 @@ def test_plan_tile_table():
     spec = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
                                  num_slots=1024), True)
     assert spec.multi_token == 1 and spec.tokens_per_chunk >= 2
-    assert spec.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and spec.block_v == 64
-    assert spec.waves_per_group == 4             # G * V / 64 = 4 tile units per k-head
+    assert spec.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and spec.block_k == 64
+    assert spec.waves_per_group == 4             # 2 heads x 2 wavefronts of 64 rows
     spec16 = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
                                    num_slots=1024, state_dtype=gdn.GDN_DTYPE_BF16), True)
-    assert spec16.block_v == 64 and spec16.waves_per_group == 4   # bf16 state: 64 columns too
+    assert spec16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and spec16.block_k == 64
+    for sd in (gdn.GDN_DTYPE_F32, gdn.GDN_DTYPE_BF16):   # column tiles: 64 columns either way
+        cols = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
+                                     num_slots=1024, state_dtype=sd,
+                                     kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), True)
+        assert cols.block_v == 64 and cols.waves_per_group == 4   # G * V / 64 tile units
     multi = gdn.gdn_plan(base_cfg(tokens_per_seq=4, num_tokens=16), False)
     assert multi.multi_token == 1
     # bf16 state: 16 rows per lane in the row split
     dec16 = gdn.gdn_plan(base_cfg(state_dtype=gdn.GDN_DTYPE_BF16), False)
     assert dec16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and dec16.block_k == 64   # 32 rows per lane
     # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
-    odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32), True)
+    odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32,
+                                kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), True)
     assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
     # row split with G = 3, K = V = 128: 8 waves per head, one head per group
     odd_rows = gdn.gdn_plan(base_cfg(num_v_heads=6), False)
@@ -209,6 +215,22 @@ def test_plan_tile_table():
     # forcing column tiles for a single token
     c1 = gdn.gdn_plan(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), False)
     assert c1.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and c1.block_v == 64
+
+
+def test_plan_row_split_token_loop():
+    """The row split over several tokens: 16 staged tokens of q/k (shared),
+    of v (per head) and double-buffered partial sums in LDS."""
+    R = gdn.GDN_KERNEL_ROW_SPLIT
+    pl = gdn.gdn_plan(base_cfg(kernel_family=R, tokens_per_seq=4, num_tokens=16), True)
+    assert pl.kernel_family == R and pl.multi_token == 1 and pl.tokens_per_chunk == 16
+    assert pl.block_k == 16 and pl.waves_per_group == 8 and pl.workgroups == 4 * 2 * 2
+    assert pl.lds_bytes == (2 * 16 * 128 + 1 * 16 * 128 + 2 * 8 * (2 * 128 + 4)) * 4
+    two = gdn.gdn_plan(base_cfg(kernel_family=R, tokens_per_seq=4, num_tokens=16, block_k=64), True)
+    assert two.waves_per_group == 4 and two.workgroups == 4 * 2     # two heads per workgroup
+    assert two.lds_bytes == (2 * 16 * 128 + 2 * 16 * 128 + 2 * 4 * (2 * 128 + 4)) * 4
+    # K = V = 256 would need more than 64 KiB of LDS
+    big = base_cfg(kernel_family=R, tokens_per_seq=4, num_tokens=16, head_k_dim=256, head_v_dim=256)
+    assert validate(big) == 7
 
 
 def test_plan_value_rows():
@@ -261,18 +283,22 @@ def test_plan_chunked():
     # unless intermediate states are written or a tiling override is given
     long = base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096)
     assert gdn.gdn_plan(long, False).kernel_family == gdn.GDN_KERNEL_CHUNKED
-    assert gdn.gdn_plan(long, False, True).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    assert gdn.gdn_plan(long, False, True).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     assert gdn.gdn_plan(base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096, block_v=32),
                         False).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
     at32 = base_cfg(tokens_per_seq=32, num_tokens=4 * 32)
     assert gdn.gdn_plan(at32, False).kernel_family == gdn.GDN_KERNEL_CHUNKED
     below = base_cfg(tokens_per_seq=31, num_tokens=4 * 31)
-    assert gdn.gdn_plan(below, False).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    assert gdn.gdn_plan(below, False).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     # varlen: the mean length decides (num_tokens / num_seqs)
     assert gdn.gdn_plan(base_cfg(num_tokens=4 * 40), True).kernel_family == gdn.GDN_KERNEL_CHUNKED
     # no chunked instance for K = 256: AUTO falls back without an error
     big = gdn.gdn_plan(base_cfg(head_k_dim=256, tokens_per_seq=100, num_tokens=400), False)
-    assert big.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and gdn.gdn_last_error_message() == ""
+    assert big.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and gdn.gdn_last_error_message() == ""
+    # nor a row-split token loop within the LDS budget at K = V = 256: column tiles
+    huge = gdn.gdn_plan(base_cfg(head_k_dim=256, head_v_dim=256, tokens_per_seq=100,
+                                 num_tokens=400), False)
+    assert huge.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
 
 
 def test_chunked_entry_point_validation():

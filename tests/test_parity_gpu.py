@@ -134,6 +134,69 @@ def test_row_split_thirty_two_rows_per_lane(dev, K, V):
         full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=bk)
 
 
+ROWS_TOKEN_CASES = [
+    W.Workload("rows_t5_f32", 70, 3, 5, 2, 4, 128, 128, W.ACT_F32, 5, 0.05, intermediates=True),
+    W.Workload("rows_t20_bf16", 71, 3, 20, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05,
+               intermediates=True, num_padded=1),
+    W.Workload("rows_varlen", 72, 7, 1, 2, 4, 128, 128, W.ACT_BF16, 9, 0.05, varlen=True,
+               len_range=(0, 40), num_padded=2, intermediates=True),
+    W.Workload("rows_k64_v128_g3", 73, 3, 7, 2, 6, 64, 128, W.ACT_F32, 4, 0.05,
+               intermediates=True),
+    W.Workload("rows_k256_v64", 74, 2, 17, 1, 2, 256, 64, W.ACT_BF16, 3, 0.05),
+    W.Workload("rows_k32_v32_t33", 75, 4, 33, 2, 2, 32, 32, W.ACT_F32, 5, 0.05,
+               intermediates=True),
+    W.Workload("rows_k128_v256", 76, 2, 3, 1, 2, 128, 256, W.ACT_F32, 3, 0.05,
+               intermediates=True),
+]
+
+
+@pytest.mark.parametrize("wl", ROWS_TOKEN_CASES, ids=lambda w: w.name)
+def test_row_split_token_loop(dev, wl):
+    """The row-split kernel over several tokens per sequence (fixed T and
+    cu_seqlens with empty and padded sequences, chunk boundaries at 16)."""
+    import linear_attention_recurrent_gating_amd as gdn
+    full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT)
+
+
+@pytest.mark.parametrize("rpl", [8, 16, 32])
+def test_row_split_token_loop_rows_per_lane(dev, rpl):
+    """Every rows-per-lane instance of the token loop (block_k = rpl * 2 at
+    V = 128), with intermediates."""
+    import linear_attention_recurrent_gating_amd as gdn
+    wl = W.Workload(f"rows_tokens_rpl{rpl}", 77 + rpl, 3, 6, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05,
+                    intermediates=True, num_padded=1)
+    full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=2 * rpl)
+
+
+def test_row_split_chain_bitwise(dev):
+    """A T-token row-split call equals T chained single-token row-split
+    (decode) calls bit for bit: the token loop repeats the single-token
+    kernel's arithmetic in the same order."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce("row-split chain bitwise")
+    wl = W.Workload("rows_chain", 78, 3, 6, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05, intermediates=True)
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    fam = gdn.GDN_KERNEL_ROW_SPLIT
+    pool_multi = torch.from_numpy(pool_np).to(dev)
+    out_multi, inter = run_gpu(inp, pool_multi, dev, kernel_family=fam, block_k=32)
+    pool_chain = torch.from_numpy(pool_np).to(dev)
+    T = wl.tokens_per_seq
+    for t in range(T):
+        rows = np.arange(wl.num_seqs) * T + t
+        step = W.HostInputs(wl.with_(tokens_per_seq=1, intermediates=False), inp.q[rows],
+                            inp.k[rows], inp.v[rows], inp.a[rows], inp.b[rows], inp.A_log,
+                            inp.dt_bias, inp.state_idx, None, np.ones(wl.num_seqs, np.int64),
+                            {n: x[rows] for n, x in inp.bits.items()})
+        out_t, _ = run_gpu(step, pool_chain, dev, kernel_family=fam, block_k=32)
+        assert torch.equal(out_t, out_multi[torch.from_numpy(rows).to(dev)]), f"out differs at t={t}"
+        for i in range(wl.num_seqs):
+            assert torch.equal(pool_chain[int(inp.state_idx[i])], inter[int(rows[i])]), \
+                f"state differs at t={t}, seq {i}"
+    assert torch.equal(pool_chain, pool_multi)
+
+
 def test_decode_kernel_families_agree(dev):
     """The row-split and column-tile single-token kernels differ only in the
     order of their fp32 reductions."""
@@ -172,8 +235,9 @@ def test_qwen3next_b64(dev):
     full_check(W.QWEN3NEXT_B64, dev)
 
 
-def test_spec_verify_b128_t4(dev):
-    full_check(W.SPEC_VERIFY, dev)
+@pytest.mark.parametrize("family", [0, 1], ids=["auto_row_split", "column_tiles"])
+def test_spec_verify_b128_t4(dev, family):
+    full_check(W.SPEC_VERIFY, dev, family=family)
 
 
 def test_spec_verify_weak_decay(dev):
@@ -223,9 +287,8 @@ def test_decode_b512_full_size_sampled(dev, wl):
 def test_chain_equals_multi_token_bitwise(dev):
     """A T-token call equals T chained one-token calls bit for bit (same fp32
     state both ways), and each chained state equals the intermediate.  The
-    one-token calls pass cu_seqlens so that they run the same (multi-token)
-    kernel family; the row-split decode kernel agrees only to rounding
-    (test_decode_kernel_families_agree, test_chain_through_decode_kernel)."""
+    one-token calls pass cu_seqlens, so both sides run the token-loop kernel
+    (test_row_split_chain_bitwise chains through the single-token kernel)."""
     import torch
     announce("chain bitwise")
     wl = W.Workload("chain", 50, 3, 6, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05, intermediates=True)
@@ -614,12 +677,18 @@ STATE_BF16_CASES = [
                       num_padded=2)),
     ("KV", W.Workload("bf16state_spec", 91, 6, 1, 4, 8, 128, 128, W.ACT_BF16, 8, 0.05,
                       varlen=True, len_range=(1, 20), num_padded=1, intermediates=True)),
-    ("KV", W.Workload("bf16state_cols_f32", 92, 5, 3, 2, 4, 64, 64, W.ACT_F32, 8, 0.05,
+    ("KV", W.Workload("bf16state_rows_f32", 92, 5, 3, 2, 4, 64, 64, W.ACT_F32, 8, 0.05,
                       intermediates=True)),
+    ("KV:cols", W.Workload("bf16state_cols_f32", 97, 5, 3, 2, 4, 64, 64, W.ACT_F32, 8, 0.05,
+                           intermediates=True)),
+    ("KV:cols", W.Workload("bf16state_cols_spec", 98, 6, 1, 4, 8, 128, 128, W.ACT_BF16, 8, 0.05,
+                           varlen=True, len_range=(1, 20), num_padded=1, intermediates=True)),
     ("VK", W.Workload("bf16state_vk_decode", 93, 9, 1, 4, 8, 128, 128, W.ACT_BF16, 12, 0.05)),
     ("VK", W.Workload("bf16state_vk_multi", 94, 4, 5, 2, 4, 64, 128, W.ACT_BF16, 6, 0.05,
                       intermediates=True)),
     ("KV", W.QWEN3NEXT_B64.with_(name="bf16state_qwen3next_b64", seed=95)),
+    ("KV:rows", W.Workload("bf16state_rows_spec", 96, 6, 1, 4, 8, 128, 128, W.ACT_BF16, 8, 0.05,
+                           varlen=True, len_range=(1, 20), num_padded=1, intermediates=True)),
 ]
 
 
@@ -631,10 +700,12 @@ def test_bf16_state_storage(dev, layout, wl):
     untouched slots and padded rows bit-identical."""
     import torch
     announce(f"bf16 state {wl.name} {layout}")
+    layout, _, kind = layout.partition(":")
+    family = {"rows": 2, "cols": 1}.get(kind, 0)   # GDN_KERNEL_ROW_SPLIT / _COLUMN_TILES
     inp = W.make_host_inputs(wl)
     bits, _ = W.round_to_bf16(to_layout(W.make_pool_host(wl), layout))
     pool = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    out, inter = run_gpu(inp, pool, dev, layout=layout)
+    out, inter = run_gpu(inp, pool, dev, layout=layout, kernel_family=family)
     seqs = np.arange(wl.num_seqs)
     o_ref, s_ref, i_ref, _ = oracle_on_seqs(inp, bits[np.maximum(inp.state_idx, 0)], seqs,
                                             intermediates=wl.intermediates, layout=layout)
