@@ -170,16 +170,16 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
     }
 
     if (rows) {
-        // Rows per lane, from same-box A/B runs on MI355X:
-        //   * K = V = 128 and at least 2048 (sequence, k-head) workgroups:
-        //     32 (two wavefronts per head; bs=512 decode 351 vs 361 us with 8,
-        //     the TP4 shard 99.1 vs 100.4 us, spec verify 264 vs 300 us);
-        //   * bf16 state, one token, K = V = 128: 32 as well (bs=64 31.0 vs
-        //     32.1 us with 16);
-        //   * otherwise 8 for fp32 state and for token loops (bs=64 51.2 vs
-        //     52.0 us with 32; 8 long sequences 1.67 vs 2.70 ms), 16 for a
-        //     single bf16 token.
-        // A block_k or waves_per_group override may ask for another.
+        // Rows per lane, from same-box A/B runs on MI355X (K = V = 128):
+        //   * one token: 32 with at least 2048 (sequence, k-head) workgroups
+        //     (two wavefronts per head; bs=512 351 vs 361 us with 8, the TP4
+        //     shard 99.1 vs 100.4 us) or bf16 state (bs=64 31.0 vs 32.1 us
+        //     with 16); otherwise 8 (bs=64, fp32 state: 51.2 vs 52.0 us);
+        //   * token loops: 32 from 512 workgroups on (spec verify 264 vs
+        //     300 us with 8; 64 x 16 tokens 102 vs 135 us), 8 below (8 long
+        //     sequences 1.67 vs 2.70 ms with 32).
+        // Other shapes: 8, or 16 for a single bf16 token.  A block_k or
+        // waves_per_group override may ask for another.
         int rpl_max = 0;
         if (c.block_k != 0) {
             for (int r : {16, 8, 32})
@@ -190,10 +190,11 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
         } else {
             const bool kv128 = K == 128 && V == 128;
             const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
-            const bool big_grid = static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 2048;
+            const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads;
+            const bool wide = s.multi_token ? groups >= 512 : (groups >= 2048 || bf16);
             int order[3] = {8, 16, 32};
-            if (kv128 && (big_grid || (bf16 && !s.multi_token))) {
-                order[0] = 32; order[1] = bf16 ? 16 : 8; order[2] = bf16 ? 8 : 16;
+            if (kv128 && wide) {
+                order[0] = 32; order[1] = 8; order[2] = 16;
             } else if (bf16 && !s.multi_token) {
                 order[0] = 16; order[1] = 8; order[2] = 32;
             }
