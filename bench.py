@@ -138,6 +138,13 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
         lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}")
+    # per-dispatch durations of the measured kernel from the trace records
+    recs = _csv_rows(os.path.join(prof_dir, "trace", "run_kernel_trace.csv"))
+    durs = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                     for r in recs if kernel in r["Kernel_Name"]])
+    if durs.size:
+        lines.append(f"# {kernel}: {durs.size} dispatches; median {np.median(durs):.1f} us, "
+                     f"p10 {np.percentile(durs, 10):.1f} us, p90 {np.percentile(durs, 90):.1f} us")
     with open(profile_path(kernel, workload, "kernel_trace"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
