@@ -487,9 +487,10 @@ gdn_chunk_fwd(const FusedParams p) {
         // ------------------------------------------ B: Gram tiles, D_b = (I + L_bb)^-1
         // 20 tiles: the 4 diagonal blocks of K K^T (then inverted), the 6
         // below them (L), and the 10 of Q K^T on and below the diagonal (P).
-        // With 8 or more wavefronts, wavefronts 0-3 take one diagonal block
-        // each and 4-7 share the other 16 tiles; otherwise tiles are dealt
-        // round-robin.
+        // With 8 wavefronts, wavefronts 4-7 each take one diagonal block,
+        // invert it and take one more tile, while wavefronts 0-3 take three
+        // tiles each: an inversion costs about as much as two tiles.
+        // Otherwise tiles are dealt round-robin.
         auto tile_of = [](int task, bool& isq, int& ti, int& tj) {
             isq = task >= 10;
             if (task < 4) {
@@ -600,12 +601,12 @@ gdn_chunk_fwd(const FusedParams p) {
             }
         };
         if (NW >= 8) {
-            // Eight wavefronts: wavefronts 4-7 take one diagonal block each
-            // (and invert it), and every wavefront takes two of the other 16
-            // tiles.
-            if (wave >= 4) gram_tile(wave - 4);
+            // wavefront w < 4: tiles 4+w, 8+w, 12+w; w >= 4: diagonal block
+            // w-4, then tile 12+w (16-19)
+            const bool inv = wave >= 4;
+            const int n = inv ? 2 : 3, step = inv ? 16 : 4;
 #pragma unroll 1
-            for (int task = 4 + wave; task < 20; task += 8) gram_tile(task);
+            for (int i = 0, task = inv ? wave - 4 : 4 + wave; i < n; ++i, task += step) gram_tile(task);
         } else {
 #pragma unroll 1
             for (int task = wave; task < 20; task += NW) gram_tile(task);
