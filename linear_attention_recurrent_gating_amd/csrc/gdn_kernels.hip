@@ -8,7 +8,12 @@
 // Triton kernels on those pages are prior art; this is a different design
 // built for 64-wide wavefronts.
 //
-// Work decomposition
+// This file holds the column-tile kernel (KV layout), the value-row kernels
+// (VK layout) and the standalone gating kernel of the unfused pair, with the
+// launch dispatcher.  The row-split kernels are in gdn_rows.hip, the chunked
+// kernel in gdn_chunk.hip.
+//
+// Work decomposition of the column tiles
 //   * A workgroup serves one (sequence, k-head) -- or a slice of its G v-heads
 //     when G*V/BV exceeds the wavefronts per workgroup -- so the normalised
 //     q/k of that k-head are computed once and shared through LDS by all the

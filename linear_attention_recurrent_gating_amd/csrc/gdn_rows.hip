@@ -11,9 +11,9 @@
 namespace gdn {
 namespace {
 
-// Whole rows per wavefront.  LPR = V/4 lanes cover
-// one V-column row, so each 128-bit load or store instruction of a wave moves
-// RG = 64/LPR consecutive rows: one contiguous kilobyte of the tile.  Lane l
+// Layout shared by both kernels.  LPR = V/4 lanes cover one V-column row, so
+// each 128-bit load or store instruction of a wave moves RG = 64/LPR
+// consecutive rows: one contiguous kilobyte of the tile.  Lane l
 // holds columns 4*(l % LPR)..+3 of rows kw*RPW + RG*i + l/LPR (i < RPL); the
 // K rows of a head are split over KW wavefronts.  S^T k, S^T q and k.q are
 // reduced in-lane, across the wave's row groups with permlane swaps, and
@@ -138,6 +138,9 @@ struct SingleTokenQK {
     }
 };
 
+// Single token per sequence (decode).  The small loads (q, k, gates, v) are
+// issued before the state tile, and q/k are normalised into LDS while the
+// tile streams in.
 template <int K, int V, int ACT, int RPL_MAX>
 __global__ void __launch_bounds__(kMaxThreads)
 gdn_decode_rows(const FusedParams p) {
