@@ -116,12 +116,12 @@ __device__ __forceinline__ Split4 split_tile(const f32x4& x) {
     return r;
 }
 
-// acc += A X for a 16 x 16 block A held as bf16 hi/lo rows in LDS (this lane's
-// four elements at a and a + lo_off) and X a 16-row accumulator tile of this
-// lane, both split: hi*hi + hi*lo + lo*hi.
-__device__ __forceinline__ f32x4 mma16_split(f32x4 acc, const __bf16* a, int lo_off, const Split4& x) {
-    const bf16x4 ah = *reinterpret_cast<const bf16x4*>(a);
-    const bf16x4 al = *reinterpret_cast<const bf16x4*>(a + lo_off);
+// acc += A X for a 16 x 16 block A given as bf16 hi/lo parts (this lane's
+// four elements, read from LDS by the caller ahead of the products) and X a
+// 16-row accumulator tile of this lane split the same way: hi*hi + hi*lo +
+// lo*hi.
+__device__ __forceinline__ f32x4 mma16_split(f32x4 acc, const bf16x4& ah, const bf16x4& al,
+                                             const Split4& x) {
     acc = mma16(ah, x.hi, acc);
     acc = mma16(ah, x.lo, acc);
     acc = mma16(al, x.hi, acc);
@@ -641,17 +641,23 @@ gdn_chunk_fwd(const FusedParams p) {
             Split8 so[kNT];
 #pragma unroll
             for (int ct = 0; ct < kNT; ++ct) so[ct] = operand_from_tiles(S[2 * kb][ct], S[2 * kb + 1][ct]);
+            // all operand reads of this 32-deep step first, so one LDS latency
+            // covers the step's 16 products
+            bf16x8 ak[4], aq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                ak[r] = lds_perm8(kt_a + 16 * r * KT + 32 * kb);
+                aq[r] = lds_perm8(qt_a + 16 * r * KT + 32 * kb);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int off = 16 * r * KT + 32 * kb;
-                const bf16x8 ak = lds_perm8(kt_a + off);
-                const bf16x8 aq = lds_perm8(qt_a + off);
 #pragma unroll
                 for (int ct = 0; ct < kNT; ++ct) {
-                    KS[r][ct] = mma_bf16(ak, so[ct].hi, KS[r][ct]);
-                    KS[r][ct] = mma_bf16(ak, so[ct].lo, KS[r][ct]);
-                    QS[r][ct] = mma_bf16(aq, so[ct].hi, QS[r][ct]);
-                    QS[r][ct] = mma_bf16(aq, so[ct].lo, QS[r][ct]);
+                    KS[r][ct] = mma_bf16(ak[r], so[ct].hi, KS[r][ct]);
+                    KS[r][ct] = mma_bf16(ak[r], so[ct].lo, KS[r][ct]);
+                    QS[r][ct] = mma_bf16(aq[r], so[ct].hi, QS[r][ct]);
+                    QS[r][ct] = mma_bf16(aq[r], so[ct].lo, QS[r][ct]);
                 }
                 if constexpr (P == 2) {
                     const bf16x8 akl = lds_perm8(kt_a + kC * KT + off);
@@ -702,22 +708,36 @@ gdn_chunk_fwd(const FusedParams p) {
             Split4 us[4];
 #pragma unroll
             for (int bi = 0; bi < 4; ++bi) {
+                // the block row's -L and D_b reads first
+                bf16x4 th[4], tl[4];
+#pragma unroll
+                for (int bj = 0; bj <= bi; ++bj) {
+                    th[bj] = *reinterpret_cast<const bf16x4*>(tb_a + 16 * bi * KC + 16 * bj);
+                    tl[bj] = *reinterpret_cast<const bf16x4*>(tb_a + kC * KC + 16 * bi * KC + 16 * bj);
+                }
                 f32x4 acc = R[bi][ct];
 #pragma unroll
                 for (int bj = 0; bj < bi; ++bj)   // acc += (-L_{bi,bj}) U_bj
-                    acc = mma16_split(acc, tb_a + 16 * bi * KC + 16 * bj, kC * KC, us[bj]);
+                    acc = mma16_split(acc, th[bj], tl[bj], us[bj]);
                 const Split4 as = split_tile(acc);
                 f32x4 u = {0.f, 0.f, 0.f, 0.f};
-                u = mma16_split(u, tb_a + 16 * bi * KC + 16 * bi, kC * KC, as);
+                u = mma16_split(u, th[bi], tl[bi], as);
                 U[bi][ct] = u;
                 us[bi] = split_tile(u);
             }
-            // O += P U (P lower triangular, diagonal included).
+            // O += P U (P lower triangular, diagonal included); each block
+            // row's P reads are issued before its products.
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+            for (int bi = 0; bi < 4; ++bi) {
+                bf16x4 ph[4], pl[4];
 #pragma unroll
-                for (int bj = 0; bj <= bi; ++bj)
-                    O[bi][ct] = mma16_split(O[bi][ct], pb_a + 16 * bi * KC + 16 * bj, kC * KC, us[bj]);
+                for (int bj = 0; bj <= bi; ++bj) {
+                    ph[bj] = *reinterpret_cast<const bf16x4*>(pb_a + 16 * bi * KC + 16 * bj);
+                    pl[bj] = *reinterpret_cast<const bf16x4*>(pb_a + kC * KC + 16 * bi * KC + 16 * bj);
+                }
+#pragma unroll
+                for (int bj = 0; bj <= bi; ++bj) O[bi][ct] = mma16_split(O[bi][ct], ph[bj], pl[bj], us[bj]);
+            }
         }
         const auto orr = buffer_rsrc(static_cast<char*>(p.out) + ((t0 * p.Hv + h) * int64_t(V)) * esz,
                                      (Lc - 1) * orow + V * esz);
@@ -756,14 +776,16 @@ gdn_chunk_fwd(const FusedParams p) {
             Split8 uo[kNT];
 #pragma unroll
             for (int ct = 0; ct < kNT; ++ct) uo[ct] = operand_from_tiles(U[2 * kb][ct], U[2 * kb + 1][ct]);
+            bf16x8 ah[MT];   // the step's operand reads first (one LDS latency)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) ah[mt] = lds_perm8(kc_a + 16 * mt * KC + 32 * kb);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int off = 16 * mt * KC + 32 * kb;
-                const bf16x8 ah = lds_perm8(kc_a + off);
 #pragma unroll
                 for (int ct = 0; ct < kNT; ++ct) {
-                    S[mt][ct] = mma_bf16(ah, uo[ct].hi, S[mt][ct]);
-                    S[mt][ct] = mma_bf16(ah, uo[ct].lo, S[mt][ct]);
+                    S[mt][ct] = mma_bf16(ah[mt], uo[ct].hi, S[mt][ct]);
+                    S[mt][ct] = mma_bf16(ah[mt], uo[ct].lo, S[mt][ct]);
                 }
                 if constexpr (P == 2) {
                     const bf16x8 al = lds_perm8(kc_a + K * KC + off);
