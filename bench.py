@@ -93,25 +93,32 @@ def cpu_threads() -> int:
 
 def cpu_baseline(inp, pool_rows: np.ndarray, budget_s: float):
     """The oracle on the same batch (its own copy of the gathered states),
-    repeated until about `budget_s` seconds have passed."""
+    repeated until about `budget_s` seconds have passed on all host cores,
+    then for a third of that on one core."""
     import oracle
     threads = cpu_threads()
     B = inp.wl.num_seqs
     idx = np.where(inp.state_idx >= 0, np.arange(B), -1).astype(np.int32)
     pool = np.ascontiguousarray(pool_rows, dtype=np.float32).copy()
     oracle.build(force=False)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.update(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias, pool, idx,
-                      inp.cu_seqlens, tokens_per_seq=inp.wl.tokens_per_seq, threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    updates = W.active_updates(inp) * reps
-    return {"value": updates / el, "unit": "updates/s", "cores": threads, "kind": "oracle",
+
+    def timed(nthreads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.update(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias, pool, idx,
+                          inp.cu_seqlens, tokens_per_seq=inp.wl.tokens_per_seq, threads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return W.active_updates(inp) * reps / el, reps, el
+
+    value, reps, el = timed(threads, budget_s)
+    one, reps1, el1 = timed(1, budget_s / 3)
+    return {"value": value, "unit": "updates/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole {inp.wl.name} batch ({B} sequences x {inp.wl.num_v_heads} "
-                      f"v-heads), fp64 oracle, repeated {reps}x over {el:.1f} s"}
+                      f"v-heads), fp64 oracle, repeated {reps}x over {el:.1f} s",
+            "single_core_value": one,
+            "single_core_sample": f"the same batch on 1 thread, repeated {reps1}x over {el1:.1f} s"}
 
 
 def _csv_rows(path):
