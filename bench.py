@@ -52,10 +52,16 @@ def kernel_name(info) -> str:
 
 
 def kernel_source_hash(kernel: str = "gdn_decode_rows") -> str:
+    """Hash of the sources a kernel is compiled from, with comments and runs of
+    white space removed (so editing a comment does not orphan a profile)."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES.get(kernel, DEFAULT_SOURCES):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

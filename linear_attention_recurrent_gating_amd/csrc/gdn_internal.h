@@ -45,7 +45,7 @@ struct FusedParams {
 
 // Kernel families.
 constexpr int kKindColumns = 0;  // wave = (v-head, BV-column tile); any token count
-constexpr int kKindRows = 1;     // wave = (v-head, block of whole rows); one token
+constexpr int kKindRows = 1;     // wave = (v-head, block of whole rows); any token count
 constexpr int kKindValueRows = 2;  // transposed (VK) state: wave = (v-head, block of value-rows)
 constexpr int kKindChunked = 3;    // workgroup = (sequence, v-head); 64-token chunks on MFMA
 
@@ -55,7 +55,7 @@ struct LaunchShape {
     int block_v;      // columns per wavefront
     int block_k;      // rows per wavefront
     int act;          // 0 = fp32, 1 = bf16
-    int multi_token;  // 0: one token per sequence; 1: chunked token loop
+    int multi_token;  // 0: one token per sequence; 1: token loop (kChunkTokens staged at a time)
     int waves;        // wavefronts per workgroup
     int rows_rpl_max; // row-split kernel: at most 32, 16 or 8 state rows per lane
     int chunk;        // tokens staged per chunk (1 for the single-token kernel)
@@ -63,7 +63,7 @@ struct LaunchShape {
     int lds_bytes;
 };
 
-// Tokens staged in LDS at a time by the multi-token kernel.
+// Tokens staged in LDS at a time by the per-token kernels' token loops.
 constexpr int kChunkTokens = 16;
 
 // Dynamic LDS bytes of a launch shape (V = head_v_dim).
