@@ -244,15 +244,16 @@ def test_spec_verify_weak_decay(dev):
     full_check(W.SPEC_VERIFY.with_(name="spec_verify_weak", decay="weak", seed=44), dev)
 
 
-@pytest.mark.parametrize("family", [0, 1], ids=["auto_chunked", "column_tiles"])
+@pytest.mark.parametrize("family", [0, 1, 2], ids=["auto_chunked", "column_tiles", "row_split"])
 def test_varlen_long(dev, family):
     """The long-varlen workload: AUTO takes the chunked kernel there (no
-    intermediate states, long sequences); the per-token column-tile kernel
-    is checked on it too."""
+    intermediate states, long sequences); the per-token kernels (column
+    tiles, and the row split's token loop over 2048-token sequences) are
+    checked on it too."""
     full_check(W.VARLEN_LONG, dev, family=family)
 
 
-@pytest.mark.parametrize("family", [0, 1], ids=["auto_chunked", "column_tiles"])
+@pytest.mark.parametrize("family", [0, 1, 2], ids=["auto_chunked", "column_tiles", "row_split"])
 def test_varlen_long_weak_decay(dev, family):
     full_check(W.VARLEN_LONG.with_(name="varlen_long_weak", decay="weak", seed=45), dev,
                family=family)
@@ -345,7 +346,7 @@ def test_deterministic(dev):
     wl = W.VARLEN_LONG.with_(name="det", num_seqs=3, len_range=(20, 70), seed=51)
     inp = W.make_host_inputs(wl)
     pool_np = W.make_pool_host(wl)
-    for family in (0, 1):   # chunked under AUTO (mean length >= 32), column tiles
+    for family in (0, 1, 2):   # chunked under AUTO (mean length >= 32), column tiles, row split
         p1 = torch.from_numpy(pool_np).to(dev)
         p2 = torch.from_numpy(pool_np).to(dev)
         o1, _ = run_gpu(inp, p1, dev, kernel_family=family)
