@@ -134,6 +134,18 @@ def test_row_split_thirty_two_rows_per_lane(dev, K, V):
         full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=bk)
 
 
+@pytest.mark.parametrize("K,V", ROW_SPLIT_PAIRS, ids=lambda x: str(x))
+def test_token_loop_all_head_dims(dev, K, V):
+    """Several tokens per sequence over every (K, V), with intermediates:
+    AUTO's kernel (the row split's token loop, or column tiles at
+    K = V = 256) and the column tiles, across the 16-token staging chunk."""
+    for act, seed, T in ((W.ACT_BF16, 80, 3), (W.ACT_F32, 81, 18)):
+        wl = W.Workload(f"tokens_k{K}_v{V}_{act}_t{T}", seed + K + V, 3, T, 2, 4, K, V, act, 6, 0.05,
+                        num_padded=1, intermediates=True)
+        full_check(wl, dev)
+        full_check(wl, dev, family=1)
+
+
 ROWS_TOKEN_CASES = [
     W.Workload("rows_t5_f32", 70, 3, 5, 2, 4, 128, 128, W.ACT_F32, 5, 0.05, intermediates=True),
     W.Workload("rows_t20_bf16", 71, 3, 20, 2, 4, 128, 128, W.ACT_BF16, 5, 0.05,
