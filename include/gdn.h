@@ -84,7 +84,9 @@ typedef enum gdn_dtype {
                            kernel, whose wavefronts never synchronise        */
 
 typedef struct gdn_config {
-    int32_t num_seqs;        /* B >= 0 sequences (B = 0: nothing is launched)   */
+    int32_t num_seqs;        /* B >= 0 sequences (B = 0, or num_tokens = 0:
+                                nothing is launched, read or written, and the
+                                activation pointers may be NULL)              */
     int32_t tokens_per_seq;  /* T >= 1 tokens per sequence when cu_seqlens is
                                 NULL (sequence i owns token rows [i*T, i*T+T));
                                 ignored with cu_seqlens                          */

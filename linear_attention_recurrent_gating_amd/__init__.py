@@ -143,17 +143,23 @@ def _ab_strides(a, b, N, Hv, Hk):
     """(ab_stride_tok, ab_stride_khead) of a/b given as dense [N, H_v] tensors or
     as [N, H_k, G] views (e.g. slices of a projection packed per k-head)."""
     G = Hv // Hk
-    if a.shape != b.shape or a.stride() != b.stride():
-        raise ValueError("a and b must have the same shape and strides")
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    if a.dim() not in (2, 3):
+        raise ValueError("a/b must be [N, H_v] or [N, H_k, G]")
+    if N == 0:   # nothing is read: any strides do
+        if tuple(a.shape) not in ((0, Hv), (0, Hk, G)):
+            raise ValueError(f"a/b must be [0, {Hv}] or [0, {Hk}, {G}]")
+        return 0, 0
+    if a.stride() != b.stride():
+        raise ValueError("a and b must have the same strides")
     if a.dim() == 2:
-        if tuple(a.shape) != (N, Hv) or a.stride(1) != 1:
+        if tuple(a.shape) != (N, Hv) or (Hv > 1 and a.stride(1) != 1):
             raise ValueError(f"a/b must be [{N}, {Hv}] with unit stride over heads")
         return (a.stride(0) if N > 1 else 0), 0
-    if a.dim() == 3:
-        if tuple(a.shape) != (N, Hk, G) or a.stride(2) != 1:
-            raise ValueError(f"a/b views must be [{N}, {Hk}, {G}] with unit innermost stride")
-        return (a.stride(0) if N > 1 else 0), a.stride(1)
-    raise ValueError("a/b must be [N, H_v] or [N, H_k, G]")
+    if tuple(a.shape) != (N, Hk, G) or (G > 1 and a.stride(2) != 1):
+        raise ValueError(f"a/b views must be [{N}, {Hk}, {G}] with unit innermost stride")
+    return (a.stride(0) if N > 1 else 0), (a.stride(1) if Hk > 1 else G)
 
 
 def _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
@@ -233,7 +239,8 @@ def make_config(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=
     cfg.scale = scale
     cfg.l2norm_eps = eps
     for name, t in (("q_stride_tok", q), ("k_stride_tok", q if k is None else k), ("v_stride_tok", v)):
-        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        # strides of empty tensors and of size-1 dimensions are never used
+        if t.shape[0] > 0 and (t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2])):
             raise ValueError("heads must be dense within a token (strides [*, D, 1])")
         setattr(cfg, name, t.stride(0) if t.shape[0] > 1 else 0)
     if a is not None:

@@ -393,7 +393,8 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
     if (s != GDN_OK) return s;
     s = check_ab_strides(*cfg);
     if (s != GDN_OK) return s;
-    if (cfg->num_seqs == 0) return GDN_OK;
+    // No sequence, or only zero-length ones: nothing is read or written.
+    if (cfg->num_seqs == 0 || cfg->num_tokens == 0) return GDN_OK;
     const size_t esize = cfg->act_dtype == GDN_DTYPE_F32 ? 4 : 2;
     const size_t state_align = cfg->state_dtype == GDN_DTYPE_BF16 ? 8 : 16;
     const bool pregated = g != nullptr;
@@ -426,7 +427,7 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
                                    cu_seqlens, out, intermediate_states, cfg);
     if (s != GDN_OK) return s;
     const gdn_config& c = *cfg;
-    if (c.num_seqs == 0) return GDN_OK;
+    if (c.num_seqs == 0 || c.num_tokens == 0) return GDN_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (c.flags & GDN_FLAG_DEBUG_CHECKS) {
         s = debug_check_indices(c, state_idx, cu_seqlens, st);
@@ -573,7 +574,7 @@ gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, con
                                 const gdn_config* cfg, void* stream) {
     g_last_error[0] = '\0';
     if (!g || !beta) {
-        if (cfg && cfg->num_seqs == 0) return GDN_OK;
+        if (cfg && (cfg->num_seqs == 0 || cfg->num_tokens == 0)) return GDN_OK;
         return fail(GDN_ERR_NULL_POINTER, "g and beta must not be NULL");
     }
     return run_update(q, k, v, nullptr, nullptr, nullptr, nullptr, g, beta, state_pool, state_idx,

@@ -131,6 +131,9 @@ def test_null_pointers():
 def test_empty_batch_accepts_null_pointers():
     c = base_cfg(num_seqs=0, num_tokens=0)
     assert validate(c, ptrs=[None] * 11) == gdn.GDN_OK
+    # sequences that are all zero-length (cu_seqlens all 0): nothing is read
+    c = base_cfg(num_seqs=3, num_tokens=0)
+    assert validate(c, ptrs=[None] * 11, cu=A[11]) == gdn.GDN_OK
 
 
 def test_misaligned_pointers():

@@ -1,0 +1,119 @@
+"""Seeded random configurations against the oracle: head dims, GQA ratios,
+activation and state dtypes, layouts, decode / fixed-T / varlen calls
+(empty and padded sequences included), intermediate states and every kernel
+family that serves the configuration.  Each configuration is small enough
+for the oracle to check every output, state and intermediate row."""
+import numpy as np
+import pytest
+
+from gpu_helpers import (TOL_STATE_GUARD, announce, live_rows, oracle_on_seqs, rel_err, run_gpu,
+                         to_layout, to_np, tol_for)
+from linear_attention_recurrent_gating_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NUM_CONFIGS = 160
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def _configs():
+    """(workload, layout, state dtype, kernel family) drawn from one seeded
+    generator; the list is the same on every run."""
+    rng = np.random.default_rng(20261203)
+    out = []
+    for n in range(NUM_CONFIGS):
+        K = int(rng.choice([32, 64, 128, 256]))
+        V = int(rng.choice([32, 64, 128, 256]))
+        Hk = int(rng.choice([1, 2, 3]))
+        G = int(rng.choice([1, 2, 3, 4]))
+        act = W.ACT_BF16 if rng.random() < 0.6 else W.ACT_F32
+        layout = "VK" if rng.random() < 0.3 else "KV"
+        state = "bf16" if rng.random() < 0.25 else "f32"
+        B = int(rng.integers(1, 7))
+        mode = rng.choice(["decode", "fixed", "varlen"])
+        T, varlen, len_range = 1, False, (1, 1)
+        if mode == "fixed":
+            T = int(rng.integers(2, 41))
+        elif mode == "varlen":
+            varlen, len_range = True, (0, int(rng.integers(1, 90)))
+        chunked_ok = K <= 128 and V <= 128
+        families = [0]
+        if layout == "KV":
+            families += [1, 2]
+        else:
+            families += [3]
+        if chunked_ok:
+            families += [4]
+        family = int(rng.choice(families))
+        inter = family != 4 and rng.random() < 0.4
+        padded = int(rng.integers(0, B)) if B > 1 else 0
+        wl = W.Workload(f"rand{n}_k{K}_v{V}_g{G}_{mode}", 1000 + n, B, T, Hk, Hk * G, K, V, act,
+                        B + 3, 0.05, varlen=varlen, len_range=len_range, num_padded=padded,
+                        intermediates=bool(inter), decay="weak" if rng.random() < 0.2 else "normal")
+        out.append((wl, layout, state, family))
+    return out
+
+
+CONFIGS = _configs()
+
+
+def _bits_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("wl,layout,state,family", CONFIGS,
+                         ids=[f"{c[0].name}_{c[1]}_{c[2]}_fam{c[3]}" for c in CONFIGS])
+def test_random_config(dev, wl, layout, state, family):
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    announce(f"random {wl.name} layout={layout} state={state} family={family} "
+             f"B={wl.num_seqs} H={wl.num_k_heads}/{wl.num_v_heads} T={wl.tokens_per_seq} "
+             f"varlen={wl.varlen} inter={wl.intermediates}")
+    inp = W.make_host_inputs(wl)
+    pool_np = to_layout(W.make_pool_host(wl), layout)
+    if state == "bf16":
+        bits, _ = W.round_to_bf16(pool_np)
+        pool = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        ref_rows = bits[np.maximum(inp.state_idx, 0)]
+    else:
+        pool = torch.from_numpy(pool_np).to(dev)
+        ref_rows = pool_np[np.maximum(inp.state_idx, 0)]
+    try:
+        out, inter = run_gpu(inp, pool, dev, kernel_family=family, layout=layout)
+    except gdn.GdnError as e:
+        # an explicit family without an instance for this shape must say so
+        assert family != 0 and e.status in (3, 7), str(e)
+        return
+    seqs = np.arange(wl.num_seqs)
+    o_ref, s_ref, i_ref, _ = oracle_on_seqs(inp, ref_rows, seqs, intermediates=wl.intermediates,
+                                            layout=layout)
+    live, dead = live_rows(inp)
+    out_np = to_np(out)
+    assert rel_err(out_np[live], o_ref[live]) <= tol_for(wl), "out"
+    assert np.all(np.isnan(out_np[dead])), "padded sequences wrote outputs"
+    lv = inp.state_idx >= 0
+    untouched = np.setdiff1d(np.arange(wl.num_slots), inp.state_idx[lv])
+    if state == "bf16":
+        after = pool.view(torch.int16).cpu().numpy().view(np.uint16)
+        got, ref = _bits_to_f32(after[inp.state_idx[lv]]), _bits_to_f32(s_ref[lv])
+        # one bf16 rounding of an fp32-accurate state
+        assert rel_err(got, ref) <= 2 ** -7, "bf16 state"
+        assert np.array_equal(after[untouched], bits[untouched]), "untouched slots changed"
+    else:
+        after = pool.cpu().numpy()
+        assert rel_err(after[inp.state_idx[lv]], s_ref[lv]) <= min(tol_for(wl), TOL_STATE_GUARD), "state"
+        assert np.array_equal(after[untouched], pool_np[untouched]), "untouched slots changed"
+    if wl.intermediates:
+        if state == "bf16":
+            ib = inter.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert rel_err(_bits_to_f32(ib[live]), _bits_to_f32(i_ref[live])) <= 2 ** -7
+        else:
+            inter_np = inter.cpu().numpy()
+            assert rel_err(inter_np[live], i_ref[live]) <= min(tol_for(wl), TOL_STATE_GUARD)
+            assert np.all(np.isnan(inter_np[dead])), "padded sequences wrote intermediates"
