@@ -56,7 +56,12 @@ def _configs():
         wl = W.Workload(f"rand{n}_k{K}_v{V}_g{G}_{mode}", 1000 + n, B, T, Hk, Hk * G, K, V, act,
                         B + 3, 0.05, varlen=varlen, len_range=len_range, num_padded=padded,
                         intermediates=bool(inter), decay="weak" if rng.random() < 0.2 else "normal")
-        out.append((wl, layout, state, family))
+        flags = 0
+        if inter and rng.random() < 0.3:
+            flags |= 0x1   # GDN_FLAG_NO_FINAL_WRITEBACK
+        if rng.random() < 0.25:
+            flags |= 0x2   # GDN_FLAG_DEBUG_CHECKS
+        out.append((wl, layout, state, family, flags))
     return out
 
 
@@ -67,14 +72,15 @@ def _bits_to_f32(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
-@pytest.mark.parametrize("wl,layout,state,family", CONFIGS,
-                         ids=[f"{c[0].name}_{c[1]}_{c[2]}_fam{c[3]}" for c in CONFIGS])
-def test_random_config(dev, wl, layout, state, family):
+@pytest.mark.parametrize("wl,layout,state,family,flags", CONFIGS,
+                         ids=[f"{c[0].name}_{c[1]}_{c[2]}_fam{c[3]}_fl{c[4]}" for c in CONFIGS])
+def test_random_config(dev, wl, layout, state, family, flags):
     import torch
     import linear_attention_recurrent_gating_amd as gdn
-    announce(f"random {wl.name} layout={layout} state={state} family={family} "
+    announce(f"random {wl.name} layout={layout} state={state} family={family} flags={flags} "
              f"B={wl.num_seqs} H={wl.num_k_heads}/{wl.num_v_heads} T={wl.tokens_per_seq} "
              f"varlen={wl.varlen} inter={wl.intermediates}")
+    no_final = bool(flags & gdn.GDN_FLAG_NO_FINAL_WRITEBACK)
     inp = W.make_host_inputs(wl)
     pool_np = to_layout(W.make_pool_host(wl), layout)
     if state == "bf16":
@@ -85,14 +91,14 @@ def test_random_config(dev, wl, layout, state, family):
         pool = torch.from_numpy(pool_np).to(dev)
         ref_rows = pool_np[np.maximum(inp.state_idx, 0)]
     try:
-        out, inter = run_gpu(inp, pool, dev, kernel_family=family, layout=layout)
+        out, inter = run_gpu(inp, pool, dev, kernel_family=family, layout=layout, flags=flags)
     except gdn.GdnError as e:
         # an explicit family without an instance for this shape must say so
         assert family != 0 and e.status in (3, 7), str(e)
         return
     seqs = np.arange(wl.num_seqs)
     o_ref, s_ref, i_ref, _ = oracle_on_seqs(inp, ref_rows, seqs, intermediates=wl.intermediates,
-                                            layout=layout)
+                                            no_final_writeback=no_final, layout=layout)
     live, dead = live_rows(inp)
     out_np = to_np(out)
     assert rel_err(out_np[live], o_ref[live]) <= tol_for(wl), "out"
