@@ -198,6 +198,32 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
     print("\n".join(lines + out))
 
 
+def summarize_utilization(prof_dir: str, workload: str, kernel: str, run: str):
+    """Writes profiles/<kernel>__<workload>__utilization.txt: the mean per
+    dispatch of every counter found in the rocprofv3 --pmc passes under
+    prof_dir (one subdirectory per pass)."""
+    os.makedirs(PROFILES, exist_ok=True)
+    vals, cmds = {}, []
+    for sub in sorted(os.listdir(prof_dir)):
+        path = os.path.join(prof_dir, sub, "run_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        names = set()
+        for r in _csv_rows(path):
+            if kernel in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                names.add(r["Counter_Name"])
+        cmds.append(f"# command: rocprofv3 --pmc {' '.join(sorted(names))} --output-format csv "
+                    f"-d {prof_dir}/{sub} -o run -- {run} --steps 5 --warmup 1 --cpu-budget 0")
+    lines = [f"# rocprofv3 utilization counters: {kernel}, workload {workload}", *cmds,
+             f"# kernel source sha256[:16] = {kernel_source_hash(kernel)}",
+             "# counter = mean over dispatches (dispatches)"]
+    lines += [f"{k} = {np.mean(v):.3f}   ({len(v)})" for k, v in sorted(vals.items())]
+    with open(profile_path(kernel, workload, "utilization"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,8 +254,17 @@ def main():
                     help="instead: write profiles/ summaries from rocprofv3 CSV output in DIR "
                          "(subdirectories trace, FETCH_SIZE, WRITE_SIZE, copy_FETCH_SIZE, "
                          "copy_WRITE_SIZE)")
+    ap.add_argument("--summarize-utilization", metavar="DIR",
+                    help="instead: write the profiles/ utilization summary from rocprofv3 --pmc "
+                         "passes in the subdirectories of DIR")
     ap.add_argument("--kernel", default="gdn_decode_rows", help="kernel name for --summarize-profiles")
     args = ap.parse_args()
+
+    if args.summarize_utilization:
+        run = f"python3 bench.py --workload {args.workload}" + (
+            f" --family {args.family}" if args.family else "")
+        summarize_utilization(args.summarize_utilization, args.workload, args.kernel, run)
+        return
 
     if args.summarize_profiles:
         d = args.summarize_profiles
