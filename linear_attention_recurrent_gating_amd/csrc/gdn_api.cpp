@@ -101,6 +101,166 @@ bool auto_chunked(const gdn_config& c, bool has_inter) {
     return ok;
 }
 
+// Grid-size check and LDS bytes of a filled-in per-token launch shape.
+gdn_status finish_shape(gdn::LaunchShape& s, int V) {
+    if (s.groups > INT32_MAX)
+        return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
+                    static_cast<long long>(s.groups));
+    s.lds_bytes = gdn::lds_bytes_for(s, V);
+    return GDN_OK;
+}
+
+// Value-row kernel (VK layout): wavefront units per k-head are G v-heads x
+// V/rpw row blocks; the wavefronts never synchronise, so any divisor of the
+// unit count may form a workgroup.
+gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
+        return fail(GDN_ERR_BAD_ARGUMENT, "GDN_LAYOUT_VK is served by GDN_KERNEL_VALUE_ROWS only");
+    if (c.block_v != 0 || c.block_k != 0)
+        return fail(GDN_ERR_BAD_ARGUMENT, "block_v/block_k do not apply to GDN_LAYOUT_VK");
+    const int rpw = gdn::vk_rows_per_wave(K, V);
+    if (rpw == 0)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no value-row kernel for K = %d, V = %d", K, V);
+    const int units = G * (V / rpw);
+    if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
+        return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/%d = %d",
+                    c.waves_per_group, rpw, units);
+    s.kind = gdn::kKindValueRows;
+    s.block_v = rpw;
+    s.block_k = K;
+    s.rows_rpl_max = 0;
+    s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+    s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
+    return finish_shape(s, V);
+}
+
+// Rows per lane (at most 32, 16 or 8) of the row-split kernel for a config
+// without a block_k override; 0 if no instance fits.  From same-box A/B runs
+// on MI355X (K = V = 128):
+//   * one token: 32 with at least 2048 (sequence, k-head) workgroups (two
+//     wavefronts per head; bs=512 351 vs 361 us with 8, the TP4 shard 99.1 vs
+//     100.4 us) or bf16 state (bs=64 31.0 vs 32.1 us with 16); otherwise 8
+//     (bs=64, fp32 state: 51.2 vs 52.0 us);
+//   * token loops: 32 from 512 workgroups on (spec verify 264 vs 300 us with
+//     8; 64 x 16 tokens 102 vs 135 us), 8 below (8 long sequences 1.67 vs
+//     2.70 ms with 32).
+// Other shapes: 8, or 16 for a single bf16 token.  A waves_per_group override
+// skips instances it cannot form, as does one whose single-head workgroup
+// would not fit the LDS budget.
+int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    const bool kv128 = K == 128 && V == 128;
+    const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
+    const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads;
+    const bool wide = s.multi_token ? groups >= 512 : (groups >= 2048 || bf16);
+    int order[3] = {8, 16, 32};
+    if (kv128 && wide) {
+        order[0] = 32; order[1] = 8; order[2] = 16;
+    } else if (bf16 && !s.multi_token) {
+        order[0] = 16; order[1] = 8; order[2] = 32;
+    }
+    for (int r : order) {
+        const int rpw = gdn::rows_per_wave(K, V, r);
+        if (rpw == 0) continue;
+        const int kw = K / rpw;
+        if (c.waves_per_group != 0 &&
+            (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0))
+            continue;
+        gdn::LaunchShape one = s;   // one head per workgroup must fit the LDS budget
+        one.kind = gdn::kKindRows;
+        one.block_k = rpw;
+        one.waves = kw;
+        if (gdn::lds_bytes_for(one, V) > kMaxDynamicLds) continue;
+        return r;
+    }
+    return 0;
+}
+
+// Row-split kernel (KV layout, whole V-column rows per wavefront): rows per
+// lane from block_k or the table above, then as many of the k-head's G
+// v-heads per workgroup as 8 wavefronts and the LDS budget allow.
+gdn_status row_split_shape(const gdn_config& c, gdn::LaunchShape& s) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    int rpl_max = 0;
+    if (c.block_k != 0) {
+        for (int r : {16, 8, 32})
+            if (gdn::rows_per_wave(K, V, r) == c.block_k) { rpl_max = r; break; }
+        if (!rpl_max)
+            return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
+                                              "wavefront for K = %d, V = %d", c.block_k, K, V);
+    } else {
+        rpl_max = default_rows_per_lane(c, s);
+        if (!rpl_max)
+            return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel fits K = %d, V = %d (at most 8 "
+                                              "wavefronts per head, %d bytes of LDS, waves_per_group)",
+                        K, V, kMaxDynamicLds);
+    }
+    const int rpw = gdn::rows_per_wave(K, V, rpl_max);
+    const int kw = K / rpw;
+    s.kind = gdn::kKindRows;
+    s.block_v = V;
+    s.block_k = rpw;
+    s.rows_rpl_max = rpl_max;
+    const auto lds_for = [&](int hp) {
+        s.waves = hp * kw;
+        return gdn::lds_bytes_for(s, V);
+    };
+    int heads = 0;
+    if (c.waves_per_group != 0) {
+        if (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT,
+                        "waves_per_group = %d must be a multiple of the %d wavefronts per head "
+                        "covering a divisor of G = %d heads", c.waves_per_group, kw, G);
+        heads = c.waves_per_group / kw;
+        if (lds_for(heads) > kMaxDynamicLds)
+            return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d needs %d bytes of LDS (at most "
+                                              "%d)", c.waves_per_group, lds_for(heads), kMaxDynamicLds);
+    } else {
+        // largest divisor of G within 8 waves and the LDS budget
+        for (int hp = G; hp >= 1 && !heads; --hp)
+            if (G % hp == 0 && hp * kw <= 8 && lds_for(hp) <= kMaxDynamicLds) heads = hp;
+        if (!heads)
+            return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no row-split workgroup fits the LDS budget");
+    }
+    s.waves = heads * kw;
+    s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (G / heads);
+    return finish_shape(s, V);
+}
+
+// Column-tile kernel (KV layout, K x block_v tiles per wavefront).
+gdn_status column_tiles_shape(const gdn_config& c, gdn::LaunchShape& s) {
+    const int G = c.num_v_heads / c.num_k_heads;
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    if (c.block_k != 0 && c.block_k != K)
+        return fail(GDN_ERR_BAD_ARGUMENT, "the column-tile kernel covers all K rows "
+                                          "(block_k must be 0 or K = %d)", K);
+    if (c.block_v != 0) {
+        if (c.block_v != 8 && c.block_v != 16 && c.block_v != 32 && c.block_v != 64)
+            return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d is not 8, 16, 32 or 64", c.block_v);
+        if (V % c.block_v != 0)
+            return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d does not divide V = %d", c.block_v, V);
+        if (!gdn::instance_exists(K, c.block_v))
+            return fail(GDN_ERR_BAD_ARGUMENT, "no kernel for K = %d with block_v = %d", K,
+                        c.block_v);
+    }
+    const int bv = c.block_v ? c.block_v : default_block_v(c);
+    const int units = G * (V / bv);
+    if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
+        return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/block_v = %d",
+                    c.waves_per_group, units);
+    s.kind = gdn::kKindColumns;
+    s.block_v = bv;
+    s.block_k = K;
+    s.rows_rpl_max = 0;
+    s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+    s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
+    return finish_shape(s, V);
+}
+
 // Chooses the kernel family, tile and grid of a (size-checked) config, and
 // rejects tiling overrides that have no kernel instance.  Calls that the
 // chunked kernel does not take default to the row-split kernel (one
@@ -109,7 +269,6 @@ bool auto_chunked(const gdn_config& c, bool has_inter) {
 // token 1.67 vs 2.45 ms); calls that override block_v, and shapes without a
 // row-split instance, use the column-tile kernel.
 gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::LaunchShape& s) {
-    const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
     s.K = K;
     s.act = c.act_dtype;
@@ -128,157 +287,19 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
 
     if (c.kernel_family == GDN_KERNEL_CHUNKED || auto_chunked(c, has_inter))
         return chunked_shape(c, s);
-    if (c.state_layout == GDN_LAYOUT_VK) {
-        if (c.kernel_family != GDN_KERNEL_AUTO && c.kernel_family != GDN_KERNEL_VALUE_ROWS)
-            return fail(GDN_ERR_BAD_ARGUMENT, "GDN_LAYOUT_VK is served by GDN_KERNEL_VALUE_ROWS only");
-        if (c.block_v != 0 || c.block_k != 0)
-            return fail(GDN_ERR_BAD_ARGUMENT, "block_v/block_k do not apply to GDN_LAYOUT_VK");
-        const int rpw = gdn::vk_rows_per_wave(K, V);
-        if (rpw == 0)
-            return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no value-row kernel for K = %d, V = %d", K, V);
-        // wavefront units per k-head: G v-heads x V/rpw row blocks; the
-        // wavefronts never synchronise, so any divisor may form a workgroup
-        const int units = G * (V / rpw);
-        if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
-            return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/%d = %d",
-                        c.waves_per_group, rpw, units);
-        s.kind = gdn::kKindValueRows;
-        s.block_v = rpw;
-        s.block_k = K;
-        s.rows_rpl_max = 0;
-        s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
-        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
-        if (s.groups > INT32_MAX)
-            return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
-                        static_cast<long long>(s.groups));
-        s.lds_bytes = gdn::lds_bytes_for(s, V);
-        return GDN_OK;
-    }
+    if (c.state_layout == GDN_LAYOUT_VK)
+        return value_rows_shape(c, s);
     if (c.kernel_family == GDN_KERNEL_VALUE_ROWS)
         return fail(GDN_ERR_BAD_ARGUMENT, "GDN_KERNEL_VALUE_ROWS needs GDN_LAYOUT_VK");
-
-    bool rows;
     if (c.kernel_family == GDN_KERNEL_ROW_SPLIT) {
         if (c.block_v != 0 && c.block_v != V)
             return fail(GDN_ERR_BAD_ARGUMENT, "the row-split kernel covers all V columns "
                                               "(block_v must be 0 or V = %d)", V);
-        rows = true;
-    } else if (c.kernel_family == GDN_KERNEL_COLUMN_TILES) {
-        rows = false;
-    } else {
-        rows = c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0;
+        return row_split_shape(c, s);
     }
-
-    if (rows) {
-        // Rows per lane, from same-box A/B runs on MI355X (K = V = 128):
-        //   * one token: 32 with at least 2048 (sequence, k-head) workgroups
-        //     (two wavefronts per head; bs=512 351 vs 361 us with 8, the TP4
-        //     shard 99.1 vs 100.4 us) or bf16 state (bs=64 31.0 vs 32.1 us
-        //     with 16); otherwise 8 (bs=64, fp32 state: 51.2 vs 52.0 us);
-        //   * token loops: 32 from 512 workgroups on (spec verify 264 vs
-        //     300 us with 8; 64 x 16 tokens 102 vs 135 us), 8 below (8 long
-        //     sequences 1.67 vs 2.70 ms with 32).
-        // Other shapes: 8, or 16 for a single bf16 token.  A block_k or
-        // waves_per_group override may ask for another.
-        int rpl_max = 0;
-        if (c.block_k != 0) {
-            for (int r : {16, 8, 32})
-                if (gdn::rows_per_wave(K, V, r) == c.block_k) { rpl_max = r; break; }
-            if (!rpl_max)
-                return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
-                                                  "wavefront for K = %d, V = %d", c.block_k, K, V);
-        } else {
-            const bool kv128 = K == 128 && V == 128;
-            const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
-            const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads;
-            const bool wide = s.multi_token ? groups >= 512 : (groups >= 2048 || bf16);
-            int order[3] = {8, 16, 32};
-            if (kv128 && wide) {
-                order[0] = 32; order[1] = 8; order[2] = 16;
-            } else if (bf16 && !s.multi_token) {
-                order[0] = 16; order[1] = 8; order[2] = 32;
-            }
-            for (int r : order) {
-                const int rpw = gdn::rows_per_wave(K, V, r);
-                if (rpw == 0) continue;
-                const int kw = K / rpw;
-                if (c.waves_per_group != 0 &&
-                    (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0))
-                    continue;
-                gdn::LaunchShape one = s;   // one head per workgroup must fit the LDS budget
-                one.kind = gdn::kKindRows;
-                one.block_k = rpw;
-                one.waves = kw;
-                if (gdn::lds_bytes_for(one, V) > kMaxDynamicLds) continue;
-                rpl_max = r;
-                break;
-            }
-            if (!rpl_max)
-                return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel fits K = %d, V = %d (at most 8 "
-                                                  "wavefronts per head, %d bytes of LDS, waves_per_group)",
-                            K, V, kMaxDynamicLds);
-        }
-        const int rpw = gdn::rows_per_wave(K, V, rpl_max);
-        if (rpw == 0)
-            return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel for K = %d, V = %d", K, V);
-        const int kw = K / rpw;
-        s.kind = gdn::kKindRows;
-        s.block_v = V;
-        s.block_k = rpw;
-        s.rows_rpl_max = rpl_max;
-        const auto lds_for = [&](int hp) {
-            s.waves = hp * kw;
-            return gdn::lds_bytes_for(s, V);
-        };
-        int heads = 0;
-        if (c.waves_per_group != 0) {
-            if (c.waves_per_group % kw != 0 || G % (c.waves_per_group / kw) != 0)
-                return fail(GDN_ERR_BAD_ARGUMENT,
-                            "waves_per_group = %d must be a multiple of the %d wavefronts per head "
-                            "covering a divisor of G = %d heads", c.waves_per_group, kw, G);
-            heads = c.waves_per_group / kw;
-            if (lds_for(heads) > kMaxDynamicLds)
-                return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d needs %d bytes of LDS (at most "
-                                                  "%d)", c.waves_per_group, lds_for(heads), kMaxDynamicLds);
-        } else {
-            // largest divisor of G within 8 waves and the LDS budget
-            for (int hp = G; hp >= 1 && !heads; --hp)
-                if (G % hp == 0 && hp * kw <= 8 && lds_for(hp) <= kMaxDynamicLds) heads = hp;
-            if (!heads)
-                return fail(GDN_ERR_UNSUPPORTED_SHAPE, "no row-split workgroup fits the LDS budget");
-        }
-        s.waves = heads * kw;
-        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (G / heads);
-    } else {
-        if (c.block_k != 0 && c.block_k != K)
-            return fail(GDN_ERR_BAD_ARGUMENT, "the column-tile kernel covers all K rows "
-                                              "(block_k must be 0 or K = %d)", K);
-        if (c.block_v != 0) {
-            if (c.block_v != 8 && c.block_v != 16 && c.block_v != 32 && c.block_v != 64)
-                return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d is not 8, 16, 32 or 64", c.block_v);
-            if (V % c.block_v != 0)
-                return fail(GDN_ERR_BAD_ARGUMENT, "block_v = %d does not divide V = %d", c.block_v, V);
-            if (!gdn::instance_exists(K, c.block_v))
-                return fail(GDN_ERR_BAD_ARGUMENT, "no kernel for K = %d with block_v = %d", K,
-                            c.block_v);
-        }
-        const int bv = c.block_v ? c.block_v : default_block_v(c);
-        const int units = G * (V / bv);
-        if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
-            return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/block_v = %d",
-                        c.waves_per_group, units);
-        s.kind = gdn::kKindColumns;
-        s.block_v = bv;
-        s.block_k = K;
-        s.rows_rpl_max = 0;
-        s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
-        s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
-    }
-    if (s.groups > INT32_MAX)
-        return fail(GDN_ERR_BAD_SHAPE, "grid of %lld workgroups is too large",
-                    static_cast<long long>(s.groups));
-    s.lds_bytes = gdn::lds_bytes_for(s, V);
-    return GDN_OK;
+    if (c.kernel_family == GDN_KERNEL_AUTO && c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0)
+        return row_split_shape(c, s);
+    return column_tiles_shape(c, s);
 }
 
 gdn_status check_config(const gdn_config* cfg, bool has_cu, bool has_inter) {
