@@ -158,6 +158,16 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
     if durs.size:
         lines.append(f"# {kernel}: {durs.size} dispatches; median {np.median(durs):.1f} us, "
                      f"p10 {np.percentile(durs, 10):.1f} us, p90 {np.percentile(durs, 90):.1f} us")
+    # the dispatch resources rocprofv3 records, as printed (VGPR_Count is in
+    # 4-register units of the 8-register wave64 allocation granule, and
+    # LDS_Block_Size leaves out the dynamic LDS of the launch)
+    res = sorted({(r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"],
+                   r["Scratch_Size"], r["Workgroup_Size_X"], r["Grid_Size_X"])
+                  for r in recs if kernel in r["Kernel_Name"]})
+    for v, a, sg, lds, scr, wg, grid in res:
+        lines.append(f"# {kernel} dispatch fields: VGPR_Count {v} (= {2 * int(v)} VGPRs allocated), "
+                     f"Accum_VGPR_Count {a}, SGPR_Count {sg}, Scratch_Size {scr}, "
+                     f"LDS_Block_Size {lds}, Workgroup_Size {wg}, Grid_Size {grid}")
     with open(profile_path(kernel, workload, "kernel_trace"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
