@@ -31,6 +31,10 @@ from linear_attention_recurrent_gating_amd import workloads as W  # noqa: E402
 METRIC = "state updates/sec (seq·head·token) + HBM GB/s as % of peak, bs=512 decode"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+# MI355X fp32 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2
+# (packed fp32) x 2.4 GHz.  The kernels are built without packed fp32 forms,
+# so their issue ceiling is half of it.
+VALU_FP32_PEAK_TFLOPS = 157.3
 CSRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -120,7 +124,14 @@ def cpu_baseline(inp, pool_rows: np.ndarray, budget_s: float):
 
     value, reps, el = timed(threads, budget_s)
     one, reps1, el1 = timed(1, budget_s / 3)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": value, "unit": "updates/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model,
             "sample": f"the whole {inp.wl.name} batch ({B} sequences x {inp.wl.num_v_heads} "
                       f"v-heads), fp64 oracle, repeated {reps}x over {el:.1f} s",
             "single_core_value": one,
@@ -469,6 +480,16 @@ def main():
                            "traffic": traffic,
                            "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
                            "kernel": KERNEL_NAMES[4]}
+    else:
+        # Token-by-token kernels: whichever of HBM and the fp32 VALU takes
+        # longer at its peak bounds the call (long sequences: the VALU).
+        flops = W.recurrent_flops(inp)
+        if flops / (VALU_FP32_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBS * 1e9):
+            tflops = flops / (kern_ms * 1e-3) / 1e12
+            res["roofline"] = {"bound": "alu", "achieved": tflops, "peak": VALU_FP32_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": tflops / VALU_FP32_PEAK_TFLOPS,
+                               "traffic": traffic, "algorithmic_flops": flops,
+                               "algorithmic_bytes": alg_bytes, "kernel": kernel_name(info)}
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(inp, pool_rows0, args.cpu_budget)
     print(json.dumps(res), flush=True)

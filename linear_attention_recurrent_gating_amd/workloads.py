@@ -215,6 +215,18 @@ def algorithmic_bytes(inp: HostInputs, final_writeback: bool = True, state_bytes
     return state + act + params
 
 
+FLOPS_PER_ELEMENT = 7   # per state element and token: decay 1, S^T k 2, k u^T 2, S^T q 2
+
+
+def recurrent_flops(inp: HostInputs) -> int:
+    """Flops of the token-by-token update for every live (sequence, v-head,
+    token): 7 per state element (the decay, the two reductions and the rank-1
+    update).  The gates and the q/k norms add O(K + V) per token and are not
+    counted."""
+    wl = inp.wl
+    return active_updates(inp) * wl.head_k_dim * wl.head_v_dim * FLOPS_PER_ELEMENT
+
+
 CHUNK_TOKENS = 64  # tokens per chunk of the chunked forward
 
 
