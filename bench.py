@@ -305,8 +305,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the update shards by sequence or head with no exchange; see DESIGN.md)",
+        print("bench.py measures one GPU: the library has no multi-GPU path (the update "
+              "shards by sequence or by k-head group with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
