@@ -14,6 +14,10 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libgdn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_INCLUDE = "/opt/rocm/include"
+ROCM_LIB = "/opt/rocm/lib"
+# A plain-C program that drives the C-ABI without Python (built next to the library).
+C_EXAMPLE_SRC = os.path.join(ROOT, "examples", "c_abi_decode.c")
+C_EXAMPLE = os.path.join(LIBDIR, "c_abi_decode")
 
 DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_rows.hip", "gdn_chunk.hip"]
 HOST_SOURCES = ["gdn_api.cpp"]
@@ -54,7 +58,25 @@ def build(verbose: bool = False, extra_device_flags=()) -> str:
     os.replace(tmp, LIB)
     for o in objs:
         os.remove(o)
+    build_c_example(verbose)
     return LIB
+
+
+def c_example_command(out: str = C_EXAMPLE, syntax_only: bool = False):
+    """gcc command line of the C example (C11, the HIP runtime's C API)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", ROCM_INCLUDE, C_EXAMPLE_SRC]
+    if syntax_only:
+        return cmd + ["-fsyntax-only"]
+    return cmd + ["-L", LIBDIR, "-lgdn", "-L", ROCM_LIB, "-lamdhip64", "-lm",
+                  "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + ROCM_LIB, "-o", out]
+
+
+def build_c_example(verbose: bool = False) -> str:
+    tmp = C_EXAMPLE + ".tmp"
+    _run(c_example_command(tmp), verbose)
+    os.replace(tmp, C_EXAMPLE)
+    return C_EXAMPLE
 
 
 if __name__ == "__main__":

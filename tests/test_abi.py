@@ -37,6 +37,14 @@ def test_exports_every_header_symbol():
         assert hasattr(lib, n)
 
 
+def test_header_and_c_example_compile_as_c11():
+    """include/gdn.h is a C header: the plain-C example that drives the ABI
+    compiles as C11 with every warning an error."""
+    from linear_attention_recurrent_gating_amd import build
+    r = subprocess.run(build.c_example_command(syntax_only=True), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_abi_version_and_status_strings():
     assert gdn.gdn_abi_version() == 1
     seen = set()
