@@ -127,7 +127,12 @@ typedef struct gdn_config {
                                 otherwise, with GDN_LAYOUT_KV, row split
                                 (column tiles where no row-split instance
                                 fits, or block_v is set); with GDN_LAYOUT_VK,
-                                value rows                                     */
+                                value rows.  The host sees only the mean
+                                length, so a batch with a few long sequences
+                                among many short ones should ask for
+                                GDN_KERNEL_CHUNKED itself: the per-token
+                                kernels take one dependent step per token of
+                                the longest sequence                           */
     int32_t block_v;         /* column tiles: 8, 16, 32 or 64 V-columns per
                                 wavefront (dividing V).  A non-zero value with
                                 GDN_KERNEL_AUTO selects the column tiles        */
