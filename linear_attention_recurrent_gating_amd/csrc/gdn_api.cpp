@@ -137,12 +137,13 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
 }
 
 // Rows per lane (at most 32, 16 or 8) of the row-split kernel for a config
-// without a block_k override; 0 if no instance fits.  From same-box A/B runs
-// on MI355X (K = V = 128):
-//   * one token: 32 with at least 2048 (sequence, k-head) workgroups (two
-//     wavefronts per head; bs=512 351 vs 361 us with 8, the TP4 shard 99.1 vs
-//     100.4 us) or bf16 state (bs=64 31.0 vs 32.1 us with 16); otherwise 8
-//     (bs=64, fp32 state: 51.2 vs 52.0 us);
+// without a block_k override; 0 if no instance fits.  From same-box runs on
+// MI355X (K = V = 128, state streamed from HBM):
+//   * one token: 32, for either storage type and any grid.  Against 8 rows
+//     per lane, fp32 state: bs=32 24.6 vs 27.6 us, bs=64 48.3 vs 50.8 us,
+//     bs=512 351 vs 361 us, the 4/8-head shard at bs=256 49.3 vs 53.5 us;
+//     bf16 state: bs=64 29.2 vs 31.7 us.  Below 16 sequences every choice
+//     takes the same ~14 us;
 //   * token loops: 32 from 512 workgroups on (spec verify 264 vs 300 us with
 //     8; 64 x 16 tokens 102 vs 135 us), 8 below (8 long sequences 1.67 vs
 //     2.70 ms with 32).
@@ -155,7 +156,7 @@ int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s) {
     const bool kv128 = K == 128 && V == 128;
     const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
     const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads;
-    const bool wide = s.multi_token ? groups >= 512 : (groups >= 2048 || bf16);
+    const bool wide = s.multi_token ? groups >= 512 : true;
     int order[3] = {8, 16, 32};
     if (kv128 && wide) {
         order[0] = 32; order[1] = 8; order[2] = 16;

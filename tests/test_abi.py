@@ -175,10 +175,10 @@ def test_plan_tile_table():
     assert decode.waves_per_group == 4 and decode.threads_per_group == 256
     assert decode.workgroups == 512 * 16          # one per (sequence, k-head)
     assert decode.lds_bytes == (2 * 128 + 4 * (2 * 128 + 4)) * 4
-    # fewer than 2048 (sequence, k-head) pairs: 8 rows per lane, one head per group
+    # a smaller batch: the same tile (32 rows per lane, the k-head's two heads)
     small = gdn.gdn_plan(base_cfg(num_seqs=64, num_tokens=64, num_k_heads=16, num_v_heads=32,
                                   num_slots=1024), False)
-    assert small.block_k == 16 and small.waves_per_group == 8 and small.workgroups == 64 * 32
+    assert small.block_k == 64 and small.waves_per_group == 4 and small.workgroups == 64 * 16
     # K = V = 256 would need 16 row blocks per head: the column-tile kernel takes it
     big = gdn.gdn_plan(base_cfg(head_k_dim=256, head_v_dim=256), False)
     assert big.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and big.block_v == 32
@@ -197,17 +197,17 @@ def test_plan_tile_table():
         assert cols.block_v == 64 and cols.waves_per_group == 4   # G * V / 64 tile units
     multi = gdn.gdn_plan(base_cfg(tokens_per_seq=4, num_tokens=16), False)
     assert multi.multi_token == 1
-    # bf16 state: 16 rows per lane in the row split
+    # bf16 state: the same 32 rows per lane
     dec16 = gdn.gdn_plan(base_cfg(state_dtype=gdn.GDN_DTYPE_BF16), False)
     assert dec16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and dec16.block_k == 64   # 32 rows per lane
     # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
     odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32,
                                 kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), True)
     assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
-    # row split with G = 3, K = V = 128: 8 waves per head, one head per group
+    # row split with G = 3, K = V = 128: 2 waves per head, all three heads in a group
     odd_rows = gdn.gdn_plan(base_cfg(num_v_heads=6), False)
-    assert odd_rows.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
-    assert odd_rows.waves_per_group == 8 and odd_rows.workgroups == 4 * 2 * 3
+    assert odd_rows.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and odd_rows.block_k == 64
+    assert odd_rows.waves_per_group == 6 and odd_rows.workgroups == 4 * 2
     # 16 rows per lane when asked for four waves per workgroup
     odd4 = gdn.gdn_plan(base_cfg(num_v_heads=6, waves_per_group=4), False)
     assert odd4.block_k == 32 and odd4.workgroups == 4 * 2 * 3
@@ -220,9 +220,9 @@ def test_plan_tile_table():
     assert r16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and r16.block_k == 16
     assert r16.waves_per_group == 8 and r16.workgroups == 4 * 2 * 2
     # row split, one head per workgroup
-    r1 = gdn.gdn_plan(base_cfg(waves_per_group=4), False)
-    assert r1.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and r1.block_k == 32
-    assert r1.waves_per_group == 4 and r1.workgroups == 4 * 2 * 2
+    r1 = gdn.gdn_plan(base_cfg(waves_per_group=2), False)
+    assert r1.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and r1.block_k == 64
+    assert r1.waves_per_group == 2 and r1.workgroups == 4 * 2 * 2
     # forcing column tiles for a single token
     c1 = gdn.gdn_plan(base_cfg(kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), False)
     assert c1.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and c1.block_v == 64
