@@ -139,6 +139,18 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _stream_handle(stream, device) -> int:
+    """The hipStream_t to enqueue on: ``stream`` (a torch stream or a raw
+    handle), else torch's current stream on ``device``."""
+    if stream is None:
+        import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:   # same handle as current_stream().cuda_stream, without the object
+            return raw(device.index if device.index is not None else torch.cuda.current_device())
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
 def _ab_strides(a, b, N, Hv, Hk):
     """(ab_stride_tok, ab_stride_khead) of a/b given as dense [N, H_v] tensors or
     as [N, H_k, G] views (e.g. slices of a projection packed per k-head)."""
@@ -275,15 +287,52 @@ def gdn_gating_delta_rule_update(q, k, v, a, b, A_log, dt_bias, state_pool, stat
                       scale=scale, eps=eps, flags=flags, kernel_family=kernel_family,
                       block_v=block_v, block_k=block_k, waves_per_group=waves_per_group, k=k,
                       state_layout=state_layout, a=a, b=b)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q.device)
     _check(raw_library().gdn_gating_delta_rule_update(
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out),
         _ptr(intermediate_states), ctypes.byref(cfg), stream))
     return out
+
+
+class PreparedUpdate:
+    """gdn_gating_delta_rule_update with its tensors bound once.  The checks,
+    the config and the pointers are computed here, so each call only
+    enqueues the launch: about 4 us of host time against 14 us for the
+    function (measured at B = 1 on MI355X).  Meant for loops that reuse the
+    same buffers: the contents of every tensor (state_idx and cu_seqlens
+    included) may change between calls, their storage, shapes and strides
+    may not.  The object holds references to the tensors."""
+
+    def __init__(self, q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens=None,
+                 out=None, intermediate_states=None, *, tokens_per_seq=None, scale: float = 0.0,
+                 eps: float = 1e-6, flags: int = 0, kernel_family: int = 0, block_v: int = 0,
+                 block_k: int = 0, waves_per_group: int = 0, state_layout=GDN_LAYOUT_KV):
+        import torch
+        if out is None:
+            out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+        _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
+                       intermediate_states, state_layout)
+        self.cfg = make_config(q, v, state_pool, state_idx, cu_seqlens,
+                               tokens_per_seq=tokens_per_seq, scale=scale, eps=eps, flags=flags,
+                               kernel_family=kernel_family, block_v=block_v, block_k=block_k,
+                               waves_per_group=waves_per_group, k=k, state_layout=state_layout,
+                               a=a, b=b)
+        self.out = out
+        self._tensors = (q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out,
+                         intermediate_states)
+        self._device = q.device
+        ptrs = [None if t is None else ctypes.c_void_p(t.data_ptr()) for t in self._tensors]
+        lib = raw_library()
+        _check(lib.gdn_validate(*ptrs, ctypes.byref(self.cfg)))
+        self._fn = lib.gdn_gating_delta_rule_update
+        self._args = (*ptrs, ctypes.byref(self.cfg))
+
+    def __call__(self, stream=None):
+        """Enqueue the update on ``stream`` (default: torch's current stream);
+        returns ``out``."""
+        _check(self._fn(*self._args, _stream_handle(stream, self._device)))
+        return self.out
 
 
 def gdn_chunk_gated_delta_rule_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx,
@@ -300,10 +349,7 @@ def gdn_chunk_gated_delta_rule_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, st
                    state_layout)
     cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
                       scale=scale, eps=eps, flags=flags, k=k, state_layout=state_layout, a=a, b=b)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q.device)
     _check(raw_library().gdn_chunk_gated_delta_rule_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out), ctypes.byref(cfg), stream))
@@ -343,10 +389,7 @@ def gdn_gating(a, b, A_log, dt_bias, g=None, beta=None, *, num_k_heads=None, str
     else:
         raise TypeError(f"a/b must be float32 or bfloat16, got {a.dtype}")
     cfg.ab_stride_tok, cfg.ab_stride_khead = _ab_strides(a, b, N, Hv, Hk)
-    if stream is None:
-        stream = torch.cuda.current_stream(a.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, a.device)
     _check(raw_library().gdn_gating(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g),
                                     _ptr(beta), ctypes.byref(cfg), stream))
     return g, beta
@@ -374,10 +417,7 @@ def gdn_recurrent_update(q, k, v, g, beta, state_pool, state_idx, cu_seqlens=Non
                       scale=scale, eps=eps, flags=flags, kernel_family=kernel_family,
                       block_v=block_v, block_k=block_k, waves_per_group=waves_per_group, k=k,
                       state_layout=state_layout)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q.device)
     _check(raw_library().gdn_recurrent_update(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(state_idx),
         _ptr(cu_seqlens), _ptr(out), _ptr(intermediate_states), ctypes.byref(cfg), stream))
