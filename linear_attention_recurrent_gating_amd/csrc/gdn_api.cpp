@@ -86,15 +86,25 @@ gdn_status chunked_shape(const gdn_config& c, gdn::LaunchShape& s) {
 }
 
 // GDN_KERNEL_AUTO takes the chunked kernel for calls that write no
-// intermediate states and average at least kChunkedMinMeanTokens tokens per
-// sequence (measured on MI355X: from 32 tokens on, its 64-token chunks beat
-// the per-token loop), when it has an instance for the shape.
+// intermediate states, when it has an instance for the shape, and the
+// sequences average at least
+//   * 32 tokens: its 64-token chunks beat the per-token loop from there on
+//     (MI355X, H 16/32, K = V = 128: 64 x 32 tokens 120 vs 164 us, 256 x 32
+//     443 vs 567 us; 64 x 16 118 vs 98 us the other way), or
+//   * 16 tokens when the (sequence, v-head) workgroups fit one per CU: the
+//     chunks then run as one wave (8 x 16 tokens 18.6 vs 23.2 us; 16 x 16
+//     34.4 vs 34.6 us, two waves, is a tie).
 constexpr int64_t kChunkedMinMeanTokens = 32;
+constexpr int64_t kChunkedMinMeanTokensOneWave = 16;
+constexpr int64_t kComputeUnits = 256;
 
 bool auto_chunked(const gdn_config& c, bool has_inter) {
     if (c.kernel_family != GDN_KERNEL_AUTO || has_inter) return false;
     if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0) return false;
-    if (c.num_seqs <= 0 || c.num_tokens < kChunkedMinMeanTokens * c.num_seqs) return false;
+    if (c.num_seqs <= 0) return false;
+    const bool one_wave = static_cast<int64_t>(c.num_seqs) * c.num_v_heads <= kComputeUnits;
+    const int64_t min_mean = one_wave ? kChunkedMinMeanTokensOneWave : kChunkedMinMeanTokens;
+    if (c.num_tokens < min_mean * c.num_seqs) return false;
     gdn::LaunchShape probe{};
     const bool ok = chunked_shape(c, probe) == GDN_OK;
     g_last_error[0] = '\0';
@@ -145,18 +155,23 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
 //     bf16 state: bs=64 29.2 vs 31.7 us.  Below 16 sequences every choice
 //     takes the same ~14 us;
 //   * token loops: 32 from 512 workgroups on (spec verify 264 vs 300 us with
-//     8; 64 x 16 tokens 102 vs 135 us), 8 below (8 long sequences 1.67 vs
-//     2.70 ms with 32).
+//     8; 64 x 16 tokens 102 vs 135 us), and from 256 when intermediate states
+//     are written for 8 or more tokens per sequence (16 x 16 tokens: fp32
+//     state 110 vs 119 us, bf16 52 vs 67 us); 8 otherwise (8 long sequences
+//     1.67 vs 2.70 ms with 32; 16 x 4 tokens with intermediates, bf16 state,
+//     22.1 vs 22.9 us).
 // Other shapes: 8, or 16 for a single bf16 token.  A waves_per_group override
 // skips instances it cannot form, as does one whose single-head workgroup
 // would not fit the LDS budget.
-int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s) {
+int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool has_inter) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
     const bool kv128 = K == 128 && V == 128;
     const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
     const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads;
-    const bool wide = s.multi_token ? groups >= 512 : true;
+    const bool long_inter =
+        has_inter && c.num_seqs > 0 && c.num_tokens >= 8 * static_cast<int64_t>(c.num_seqs);
+    const bool wide = s.multi_token ? (groups >= 512 || (long_inter && groups >= 256)) : true;
     int order[3] = {8, 16, 32};
     if (kv128 && wide) {
         order[0] = 32; order[1] = 8; order[2] = 16;
@@ -183,7 +198,7 @@ int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s) {
 // Row-split kernel (KV layout, whole V-column rows per wavefront): rows per
 // lane from block_k or the table above, then as many of the k-head's G
 // v-heads per workgroup as 8 wavefronts and the LDS budget allow.
-gdn_status row_split_shape(const gdn_config& c, gdn::LaunchShape& s) {
+gdn_status row_split_shape(const gdn_config& c, bool has_inter, gdn::LaunchShape& s) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
     int rpl_max = 0;
@@ -194,7 +209,7 @@ gdn_status row_split_shape(const gdn_config& c, gdn::LaunchShape& s) {
             return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel with block_k = %d rows per "
                                               "wavefront for K = %d, V = %d", c.block_k, K, V);
     } else {
-        rpl_max = default_rows_per_lane(c, s);
+        rpl_max = default_rows_per_lane(c, s, has_inter);
         if (!rpl_max)
             return fail(GDN_ERR_BAD_ARGUMENT, "no row-split kernel fits K = %d, V = %d (at most 8 "
                                               "wavefronts per head, %d bytes of LDS, waves_per_group)",
@@ -296,10 +311,10 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
         if (c.block_v != 0 && c.block_v != V)
             return fail(GDN_ERR_BAD_ARGUMENT, "the row-split kernel covers all V columns "
                                               "(block_v must be 0 or V = %d)", V);
-        return row_split_shape(c, s);
+        return row_split_shape(c, has_inter, s);
     }
     if (c.kernel_family == GDN_KERNEL_AUTO && c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0)
-        return row_split_shape(c, s);
+        return row_split_shape(c, has_inter, s);
     return column_tiles_shape(c, s);
 }
 

@@ -242,6 +242,17 @@ def test_plan_row_split_token_loop():
     # K = V = 256 would need more than 64 KiB of LDS
     big = base_cfg(kernel_family=R, tokens_per_seq=4, num_tokens=16, head_k_dim=256, head_v_dim=256)
     assert validate(big) == 7
+    # rows per lane of the token loop: 32 from 512 (sequence, k-head) workgroups,
+    # or from 256 when intermediate states are written for >= 8 tokens per
+    # sequence; 8 below
+    heads = dict(num_k_heads=16, num_v_heads=32)
+    def bk(B, T, inter):
+        cfg = base_cfg(num_seqs=B, tokens_per_seq=T, num_tokens=B * T, num_slots=B, **heads)
+        return gdn.gdn_plan(cfg, False, inter).block_k
+    assert bk(32, 4, False) == 64 and bk(32, 4, True) == 64
+    assert bk(16, 4, False) == 16 and bk(16, 4, True) == 16 and bk(16, 7, True) == 16
+    assert bk(16, 8, True) == 64 and bk(16, 16, True) == 64
+    assert bk(8, 16, True) == 16
 
 
 def test_plan_value_rows():
@@ -297,10 +308,21 @@ def test_plan_chunked():
     assert gdn.gdn_plan(long, False, True).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     assert gdn.gdn_plan(base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096, block_v=32),
                         False).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
-    at32 = base_cfg(tokens_per_seq=32, num_tokens=4 * 32)
+    # more (sequence, v-head) workgroups than CUs: from 32 tokens on
+    wide = dict(num_seqs=128, num_k_heads=16, num_v_heads=32, num_slots=256)
+    at32 = base_cfg(tokens_per_seq=32, num_tokens=128 * 32, **wide)
     assert gdn.gdn_plan(at32, False).kernel_family == gdn.GDN_KERNEL_CHUNKED
-    below = base_cfg(tokens_per_seq=31, num_tokens=4 * 31)
+    below = base_cfg(tokens_per_seq=31, num_tokens=128 * 31, **wide)
     assert gdn.gdn_plan(below, False).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
+    # at most one workgroup per CU (256): from 16 tokens on
+    one_wave = dict(num_seqs=8, num_k_heads=16, num_v_heads=32, num_slots=16)
+    assert gdn.gdn_plan(base_cfg(tokens_per_seq=16, num_tokens=8 * 16, **one_wave),
+                        False).kernel_family == gdn.GDN_KERNEL_CHUNKED
+    assert gdn.gdn_plan(base_cfg(tokens_per_seq=15, num_tokens=8 * 15, **one_wave),
+                        False).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
+    nine = dict(one_wave, num_seqs=9)     # 288 workgroups: the 32-token rule again
+    assert gdn.gdn_plan(base_cfg(tokens_per_seq=16, num_tokens=9 * 16, **nine),
+                        False).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     # varlen: the mean length decides (num_tokens / num_seqs)
     assert gdn.gdn_plan(base_cfg(num_tokens=4 * 40), True).kernel_family == gdn.GDN_KERNEL_CHUNKED
     # no chunked instance for K = 256: AUTO falls back without an error
