@@ -123,7 +123,9 @@ typedef struct gdn_config {
      * order of the fp32 reductions, never the operation. */
     int32_t kernel_family;   /* GDN_KERNEL_AUTO (0): the chunked kernel for
                                 calls without intermediate states averaging at
-                                least 32 tokens per sequence (K, V <= 128);
+                                least 32 tokens per sequence, or 16 when the
+                                num_seqs * H_v workgroups fit one per CU
+                                (256) (K, V <= 128);
                                 otherwise, with GDN_LAYOUT_KV, row split
                                 (column tiles where no row-split instance
                                 fits, or block_v is set); with GDN_LAYOUT_VK,
