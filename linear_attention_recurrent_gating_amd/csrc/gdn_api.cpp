@@ -160,9 +160,12 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
 //     state 110 vs 119 us, bf16 52 vs 67 us); 8 otherwise (8 long sequences
 //     1.67 vs 2.70 ms with 32; 16 x 4 tokens with intermediates, bf16 state,
 //     22.1 vs 22.9 us).
-// Other shapes: 8, or 16 for a single bf16 token.  A waves_per_group override
-// skips instances it cannot form, as does one whose single-head workgroup
-// would not fit the LDS budget.
+// Other shapes: one token, 32 with fp32 state (bs=64: K = 64, V = 128 25.8
+// vs 29.1 us with 8; K = V = 256 184.5 us, where the column tiles take
+// 200.8; bs=512 within 3% of the best); with bf16 state 32 below 2048
+// workgroups for K, V <= 128 (bs=64, K = 128, V = 64: 15.1 vs 16.8 us with
+// 16), else 16 (bs=512: 102.8 vs 107.2 us with 32); token loops, 8.  A waves_per_group override skips instances it cannot form, as does one
+// whose single-head workgroup would not fit the LDS budget.
 int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool has_inter) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
@@ -175,7 +178,9 @@ int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool h
     int order[3] = {8, 16, 32};
     if (kv128 && wide) {
         order[0] = 32; order[1] = 8; order[2] = 16;
-    } else if (bf16 && !s.multi_token) {
+    } else if (!s.multi_token && (!bf16 || (groups < 2048 && K <= 128 && V <= 128))) {
+        order[0] = 32; order[1] = 16; order[2] = 8;
+    } else if (!s.multi_token) {
         order[0] = 16; order[1] = 8; order[2] = 32;
     }
     for (int r : order) {
@@ -313,7 +318,8 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
                                               "(block_v must be 0 or V = %d)", V);
         return row_split_shape(c, has_inter, s);
     }
-    if (c.kernel_family == GDN_KERNEL_AUTO && c.block_v == 0 && gdn::rows_per_wave(K, V, 16) > 0)
+    if (c.kernel_family == GDN_KERNEL_AUTO && c.block_v == 0 &&
+        (c.block_k != 0 || default_rows_per_lane(c, s, has_inter) > 0))
         return row_split_shape(c, has_inter, s);
     return column_tiles_shape(c, s);
 }

@@ -179,9 +179,19 @@ def test_plan_tile_table():
     small = gdn.gdn_plan(base_cfg(num_seqs=64, num_tokens=64, num_k_heads=16, num_v_heads=32,
                                   num_slots=1024), False)
     assert small.block_k == 64 and small.waves_per_group == 4 and small.workgroups == 64 * 16
-    # K = V = 256 would need 16 row blocks per head: the column-tile kernel takes it
+    # K = V = 256, one token: 32 rows per lane, 8 wavefronts per head (one
+    # 256-float row per instruction)
     big = gdn.gdn_plan(base_cfg(head_k_dim=256, head_v_dim=256), False)
-    assert big.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and big.block_v == 32
+    assert big.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and big.block_k == 32
+    assert big.waves_per_group == 8 and big.workgroups == 4 * 2 * 2
+    # other shapes, one token: 32 rows per lane with fp32 state, 16 with bf16
+    k64 = gdn.gdn_plan(base_cfg(head_k_dim=64), False)       # V = 128: 2 rows per instruction
+    assert k64.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and k64.block_k == 64
+    k64b = gdn.gdn_plan(base_cfg(head_k_dim=64, state_dtype=gdn.GDN_DTYPE_BF16), False)
+    assert k64b.block_k == 64        # a small grid: 32 rows per lane with bf16 state too
+    k64w = gdn.gdn_plan(base_cfg(head_k_dim=64, state_dtype=gdn.GDN_DTYPE_BF16, num_seqs=1024,
+                                 num_tokens=1024, num_slots=1024), False)
+    assert k64w.block_k == 32        # 2048 workgroups: 16 rows per lane
     spec = gdn.gdn_plan(base_cfg(num_seqs=128, num_tokens=512, num_k_heads=16, num_v_heads=32,
                                  num_slots=1024), True)
     assert spec.multi_token == 1 and spec.tokens_per_chunk >= 2
