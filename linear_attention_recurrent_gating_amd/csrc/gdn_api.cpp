@@ -164,8 +164,13 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
 // vs 29.1 us with 8; K = V = 256 184.5 us, where the column tiles take
 // 200.8; bs=512 within 3% of the best); with bf16 state 32 below 2048
 // workgroups for K, V <= 128 (bs=64, K = 128, V = 64: 15.1 vs 16.8 us with
-// 16), else 16 (bs=512: 102.8 vs 107.2 us with 32); token loops, 8.  A waves_per_group override skips instances it cannot form, as does one
-// whose single-head workgroup would not fit the LDS budget.
+// 16), else 16 (bs=512: 102.8 vs 107.2 us with 32).  Token loops: 32 at
+// K = 256, V = 128 (256 x 16 tokens: 641 vs 900 us with 16); 16 with
+// intermediate states and fp32 state where K or V is 64 (256 x 4: 304 vs
+// 336 us with 8); else 8.  (Without intermediate states the column tiles
+// take those shapes from 1024 workgroups on; see plan_launch.)  A
+// waves_per_group override skips instances it cannot form, as does one whose
+// single-head workgroup would not fit the LDS budget.
 int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool has_inter) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
@@ -181,6 +186,10 @@ int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool h
     } else if (!s.multi_token && (!bf16 || (groups < 2048 && K <= 128 && V <= 128))) {
         order[0] = 32; order[1] = 16; order[2] = 8;
     } else if (!s.multi_token) {
+        order[0] = 16; order[1] = 8; order[2] = 32;
+    } else if (K == 256 && V == 128) {
+        order[0] = 32; order[1] = 16; order[2] = 8;
+    } else if (has_inter && !bf16 && K <= 128 && V <= 128 && !kv128) {
         order[0] = 16; order[1] = 8; order[2] = 32;
     }
     for (int r : order) {
@@ -282,6 +291,18 @@ gdn_status column_tiles_shape(const gdn_config& c, gdn::LaunchShape& s) {
     return finish_shape(s, V);
 }
 
+// Token loops without intermediate states at K, V <= 128 other than
+// K = V = 128, with at least 1024 (sequence, k-head) workgroups: the column
+// tiles beat every row split (MI355X, H 16/32: K = 128, V = 64, 256 x 16
+// tokens 178.5 vs 182.7 us at 16 rows per lane and 253.6 at 8; K = 64,
+// V = 128, 64 x 4 tokens 26.6 vs 31.1 us), within 6% of the best everywhere.
+bool prefer_column_tiles(const gdn_config& c, const gdn::LaunchShape& s, bool has_inter) {
+    const int K = c.head_k_dim, V = c.head_v_dim;
+    if (!s.multi_token || has_inter || c.block_k != 0 || c.waves_per_group != 0) return false;
+    if (K > 128 || V > 128 || (K == 128 && V == 128)) return false;
+    return static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 1024;
+}
+
 // Chooses the kernel family, tile and grid of a (size-checked) config, and
 // rejects tiling overrides that have no kernel instance.  Calls that the
 // chunked kernel does not take default to the row-split kernel (one
@@ -319,7 +340,8 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
         return row_split_shape(c, has_inter, s);
     }
     if (c.kernel_family == GDN_KERNEL_AUTO && c.block_v == 0 &&
-        (c.block_k != 0 || default_rows_per_lane(c, s, has_inter) > 0))
+        (c.block_k != 0 || (!prefer_column_tiles(c, s, has_inter) &&
+                            default_rows_per_lane(c, s, has_inter) > 0)))
         return row_split_shape(c, has_inter, s);
     return column_tiles_shape(c, s);
 }

@@ -263,6 +263,19 @@ def test_plan_row_split_token_loop():
     assert bk(16, 4, False) == 16 and bk(16, 4, True) == 16 and bk(16, 7, True) == 16
     assert bk(16, 8, True) == 64 and bk(16, 16, True) == 64
     assert bk(8, 16, True) == 16
+    # other head dims
+    def plan(B, T, inter, K, V, **kw):
+        cfg = base_cfg(num_seqs=B, tokens_per_seq=T, num_tokens=B * T, num_slots=B, head_k_dim=K,
+                       head_v_dim=V, **heads, **kw)
+        return gdn.gdn_plan(cfg, False, inter)
+    assert plan(16, 4, False, 256, 128).block_k == 64        # K = 256, V = 128: 32 rows per lane
+    assert plan(16, 4, True, 64, 128).block_k == 32          # fp32 intermediates: 16 rows per lane
+    assert plan(16, 4, True, 64, 128, state_dtype=gdn.GDN_DTYPE_BF16).block_k == 16
+    # no intermediates, >= 1024 (sequence, k-head) workgroups: the column tiles
+    assert plan(64, 4, False, 128, 64).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
+    assert plan(32, 4, False, 128, 64).kernel_family == R
+    assert plan(64, 4, True, 128, 64).kernel_family == R
+    assert plan(64, 4, False, 128, 128).kernel_family == R
 
 
 def test_plan_value_rows():
