@@ -128,7 +128,11 @@ typedef struct gdn_config {
                                 (256) (K, V <= 128);
                                 otherwise, with GDN_LAYOUT_KV, row split
                                 (column tiles where no row-split instance
-                                fits, or block_v is set); with GDN_LAYOUT_VK,
+                                fits, where block_v is set, and for token
+                                loops without intermediate states at K, V <=
+                                128 other than 128 x 128 from 1024
+                                (sequence, k-head) workgroups); with
+                                GDN_LAYOUT_VK,
                                 value rows.  The host sees only the mean
                                 length, so a batch with a few long sequences
                                 among many short ones should ask for
