@@ -118,6 +118,21 @@ def test_row_split_eight_rows_per_lane(dev, K, V):
         full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, waves=kw)
 
 
+@pytest.mark.parametrize("K,V", [(64, 64), (64, 128), (128, 64), (128, 128), (128, 256),
+                                 (256, 128)], ids=lambda x: str(x))
+def test_row_split_sixteen_rows_per_lane(dev, K, V):
+    """Row split with 16 state rows per lane (block_k = 16 * rows per
+    instruction): the single-token instance for bf16 state at large grids
+    outside K = V = 128, and for fp32 intermediates at K or V = 64."""
+    import linear_attention_recurrent_gating_amd as gdn
+    rg = 64 // (V // 4)
+    bk = 16 * rg
+    for act, seed in ((W.ACT_BF16, 67), (W.ACT_F32, 68)):
+        wl = W.Workload(f"rows16_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
+                        num_padded=1)
+        full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=bk)
+
+
 @pytest.mark.parametrize("K,V", [(32, 32), (64, 64), (128, 32), (128, 64), (128, 128),
                                  (256, 64), (256, 128)], ids=lambda x: str(x))
 def test_row_split_thirty_two_rows_per_lane(dev, K, V):
