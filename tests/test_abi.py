@@ -284,6 +284,10 @@ def test_plan_value_rows():
     assert vk.kernel_family == gdn.GDN_KERNEL_VALUE_ROWS
     assert vk.block_v == 32 and vk.block_k == 128      # 32 whole value-rows per wavefront
     assert vk.waves_per_group == 8 and vk.workgroups == 512 * 16 and vk.lds_bytes == 0
+    vk16 = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, num_seqs=512, num_tokens=512,
+                                 num_k_heads=16, num_v_heads=32,
+                                 state_dtype=gdn.GDN_DTYPE_BF16), False)
+    assert vk16.waves_per_group == 4 and vk16.workgroups == 512 * 16 * 2   # bf16: 4 waves
     multi = gdn.gdn_plan(base_cfg(state_layout=gdn.GDN_LAYOUT_VK, tokens_per_seq=4,
                                   num_tokens=16), True)
     assert multi.kernel_family == gdn.GDN_KERNEL_VALUE_ROWS and multi.multi_token == 1
