@@ -33,9 +33,10 @@ bool supported_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 int default_block_v(const gdn_config& c) {
     // 64 columns (a 256-byte fp32 or 128-byte bf16 row segment, 128 state
     // VGPRs at K = 128), measured on MI355X against 32: spec verify 276 vs
-    // 300 us with fp32 state, 202 vs 237 us with bf16. Narrower where V or the
-    // instance table asks for it.
-    int bv = 64;
+    // 300 us with fp32 state, 202 vs 237 us with bf16. 32 for fp32 state at
+    // K = 128, V = 64 (64 x 4 tokens 25.8 vs 30.6 us, 256 x 16 166.8 vs
+    // 176.2 us). Narrower where V or the instance table asks for it.
+    int bv = (c.state_dtype == GDN_DTYPE_F32 && c.head_k_dim == 128 && c.head_v_dim == 64) ? 32 : 64;
     while (bv > 8 && (c.head_v_dim % bv != 0 || !gdn::instance_exists(c.head_k_dim, bv))) bv /= 2;
     return bv;
 }

@@ -276,6 +276,9 @@ def test_plan_row_split_token_loop():
     assert plan(32, 4, False, 128, 64).kernel_family == R
     assert plan(64, 4, True, 128, 64).kernel_family == R
     assert plan(64, 4, False, 128, 128).kernel_family == R
+    cols = plan(64, 4, False, 128, 64)           # fp32 state at K = 128, V = 64: 32 columns
+    assert cols.block_v == 32 and cols.waves_per_group == 4
+    assert plan(64, 4, False, 128, 64, state_dtype=gdn.GDN_DTYPE_BF16).block_v == 64
 
 
 def test_plan_value_rows():
