@@ -125,7 +125,8 @@ typedef struct gdn_config {
                                 calls without intermediate states averaging at
                                 least 32 tokens per sequence, or 16 when the
                                 num_seqs * H_v workgroups fit one per CU
-                                (256) (K, V <= 128);
+                                (256), both times sqrt(128*128 / (K*V))
+                                (K, V <= 128);
                                 otherwise, with GDN_LAYOUT_KV, row split
                                 (column tiles where no row-split instance
                                 fits, where block_v is set, and for token

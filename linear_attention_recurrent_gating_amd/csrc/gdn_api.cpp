@@ -95,16 +95,28 @@ gdn_status chunked_shape(const gdn_config& c, gdn::LaunchShape& s) {
 //   * 16 tokens when the (sequence, v-head) workgroups fit one per CU: the
 //     chunks then run as one wave (8 x 16 tokens 18.6 vs 23.2 us; 16 x 16
 //     34.4 vs 34.6 us, two waves, is a tie).
+// Both thresholds are for K x V = 128 x 128.  A smaller state makes a token
+// step cheaper, while a chunk keeps its 64 x 64 Gram and inverse, so they
+// grow as sqrt(128 * 128 / (K * V)): K = 128, V = 64 crosses over between 32
+// and 64 tokens (256 x 32: 310 us per token, 455 chunked; 256 x 64: 572 vs
+// 457), K = V = 32 beyond 64 (256 x 64: 182 vs 233 us).
 constexpr int64_t kChunkedMinMeanTokens = 32;
 constexpr int64_t kChunkedMinMeanTokensOneWave = 16;
 constexpr int64_t kComputeUnits = 256;
+
+int64_t chunked_min_mean_tokens(const gdn_config& c, int64_t base) {
+    const double kv = static_cast<double>(c.head_k_dim) * c.head_v_dim;
+    if (kv >= 128.0 * 128.0) return base;
+    return static_cast<int64_t>(std::ceil(base * std::sqrt(128.0 * 128.0 / kv)));
+}
 
 bool auto_chunked(const gdn_config& c, bool has_inter) {
     if (c.kernel_family != GDN_KERNEL_AUTO || has_inter) return false;
     if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0) return false;
     if (c.num_seqs <= 0) return false;
     const bool one_wave = static_cast<int64_t>(c.num_seqs) * c.num_v_heads <= kComputeUnits;
-    const int64_t min_mean = one_wave ? kChunkedMinMeanTokensOneWave : kChunkedMinMeanTokens;
+    const int64_t min_mean = chunked_min_mean_tokens(
+        c, one_wave ? kChunkedMinMeanTokensOneWave : kChunkedMinMeanTokens);
     if (c.num_tokens < min_mean * c.num_seqs) return false;
     gdn::LaunchShape probe{};
     const bool ok = chunked_shape(c, probe) == GDN_OK;

@@ -353,6 +353,13 @@ def test_plan_chunked():
     nine = dict(one_wave, num_seqs=9)     # 288 workgroups: the 32-token rule again
     assert gdn.gdn_plan(base_cfg(tokens_per_seq=16, num_tokens=9 * 16, **nine),
                         False).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
+    # smaller states cross over later: 32 * sqrt(128 * 128 / (K * V)) tokens
+    for (K, V), need in (((128, 64), 46), ((64, 64), 64), ((32, 32), 128)):
+        at = base_cfg(tokens_per_seq=need, num_tokens=128 * need, head_k_dim=K, head_v_dim=V, **wide)
+        assert gdn.gdn_plan(at, False).kernel_family == gdn.GDN_KERNEL_CHUNKED, (K, V)
+        less = base_cfg(tokens_per_seq=need - 1, num_tokens=128 * (need - 1), head_k_dim=K,
+                        head_v_dim=V, **wide)
+        assert gdn.gdn_plan(less, False).kernel_family != gdn.GDN_KERNEL_CHUNKED, (K, V)
     # varlen: the mean length decides (num_tokens / num_seqs)
     assert gdn.gdn_plan(base_cfg(num_tokens=4 * 40), True).kernel_family == gdn.GDN_KERNEL_CHUNKED
     # no chunked instance for K = 256: AUTO falls back without an error
