@@ -94,8 +94,9 @@ ROW_SPLIT_PAIRS = [(K, V) for K in (32, 64, 128, 256) for V in (32, 64, 128, 256
 
 @pytest.mark.parametrize("K,V", ROW_SPLIT_PAIRS, ids=lambda x: str(x))
 def test_single_token_all_head_dims(dev, K, V):
-    """Single-token decode over every supported (K, V): the row-split kernel
-    (column tiles for K = V = 256), bf16 and fp32."""
+    """Single-token decode over every supported (K, V): AUTO's row-split
+    tile for each (32 rows per lane with fp32 state, 8 wavefronts per head
+    at K = V = 256), bf16 and fp32 activations."""
     for act, seed in ((W.ACT_BF16, 60), (W.ACT_F32, 61)):
         wl = W.Workload(f"decode_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
                         num_padded=1)
