@@ -68,7 +68,7 @@ struct ChunkPlan {
     static constexpr int KT = K + 8;               // pitch of [C][K] (bf16)
     static constexpr int KC = kC + 8;              // pitch of [K][C] and [C][C] (bf16)
     static constexpr int LD = 16 + 4;              // pitch of a 16 x 16 fp32 block
-    static constexpr int kScalars = 6;             // beta, e^G, e^{G_last-G}, rk, rq, G
+    static constexpr int kScalars = 7;             // beta, e^G, e^{G_last-G}, rk, rq, G hi, G lo
     static constexpr int kt = 0;                              // P x [C][KT] raw keys
     static constexpr int qt = kt + P * kC * KT * 2;           // P x [C][KT] raw queries
     static constexpr int kc = qt + P * kC * KT * 2;           // P x [K][KC] raw keys, transposed
@@ -191,7 +191,20 @@ __device__ __forceinline__ float dpp_or_zero(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
 }
 
-__device__ __forceinline__ float wave_prefix_sum(float x) {
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_or_zero(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(b)), CTRL, ROW_MASK, 0xF, true));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(b >> 32)), CTRL, ROW_MASK, 0xF, true));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// In fp64: the chunk's log-decay prefix sums can reach thousands when a
+// token's gate saturates, and the Gram scaling needs exp(G_t - G_s) for
+// neighbouring tokens, a small difference of two large sums.
+__device__ __forceinline__ double wave_prefix_sum(double x) {
     x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
     x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
     x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
@@ -199,6 +212,13 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
     x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
     return x;
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), l));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
 // LDS written by some lanes of this wavefront becomes visible to its others.
@@ -435,12 +455,16 @@ gdn_chunk_fwd(const FusedParams p) {
                 gate_values(L.ga, L.gb, A_h, dtb_h, glog, bet);
             }
             if (lane >= Ln) glog = bet = 0.0f;  // padding tokens: no decay, no update
-            const float G = wave_prefix_sum(glog);
-            const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kWave - 1));
+            const double G = wave_prefix_sum(static_cast<double>(glog));
+            const double Glast = readlane_f64(G, kWave - 1);
+            // G as an unevaluated float pair: differences of nearby sums then
+            // come out exact in the high parts (Sterbenz) plus the low parts
+            const float Ghi = static_cast<float>(G);
             sc[lane] = bet;
-            sc[5 * kC + lane] = G;
-            sc[kC + lane] = expf(G);
-            sc[2 * kC + lane] = expf(Glast - G);
+            sc[5 * kC + lane] = Ghi;
+            sc[6 * kC + lane] = static_cast<float>(G - static_cast<double>(Ghi));
+            sc[kC + lane] = expf(Ghi);
+            sc[2 * kC + lane] = expf(static_cast<float>(Glast - G));
         }
     };
 
@@ -462,6 +486,7 @@ gdn_chunk_fwd(const FusedParams p) {
         const float* const s_rk = sc + 3 * kC;
         const float* const s_rq = sc + 4 * kC;
         const float* const s_G = sc + 5 * kC;
+        const float* const s_Glo = sc + 6 * kC;
         lds_barrier();  // chunk c is staged; the previous chunk's products are done
         // This wave's v values (accumulator row order), needed once the
         // state products are done; they land during the Gram tiles.
@@ -510,18 +535,20 @@ gdn_chunk_fwd(const FusedParams p) {
         auto tile_epilogue = [&](bool isq, int ti, int tj, const f32x4& acc) {
             // acc[e] = (X K^T)[16 ti + 4 g4 + e][16 tj + m16]
             const int s = 16 * tj + m16;
-            const float rks = s_rk[s], Gs = s_G[s];
+            const float rks = s_rk[s], Gs = s_G[s], Gls = s_Glo[s];
             const float4 G4 = *reinterpret_cast<const float4*>(s_G + 16 * ti + 4 * g4);
+            const float4 GL4 = *reinterpret_cast<const float4*>(s_Glo + 16 * ti + 4 * g4);
             const float4 B4 = *reinterpret_cast<const float4*>(s_beta + 16 * ti + 4 * g4);
             const float4 K4 = *reinterpret_cast<const float4*>(s_rk + 16 * ti + 4 * g4);
             const float4 Q4 = *reinterpret_cast<const float4*>(s_rq + 16 * ti + 4 * g4);
             const float Gt[4] = {G4.x, G4.y, G4.z, G4.w};
+            const float GLt[4] = {GL4.x, GL4.y, GL4.z, GL4.w};
             const float Bt[4] = {B4.x * K4.x, B4.y * K4.y, B4.z * K4.z, B4.w * K4.w};
             const float Qt[4] = {Q4.x, Q4.y, Q4.z, Q4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * ti + 4 * g4 + e;
-                const float f = t >= s ? expf(Gt[e] - Gs) * rks * acc[e] : 0.0f;
+                const float f = t >= s ? expf((Gt[e] - Gs) + (GLt[e] - Gls)) * rks * acc[e] : 0.0f;
                 if (isq) {
                     __bf16 hi, lo;
                     split_bf16(Qt[e] * f, hi, lo);
