@@ -124,3 +124,16 @@ def test_inputs_are_reproducible():
         assert np.array_equal(getattr(a, name), getattr(b, name)), name
     p0, p1 = W.make_pool_host(W.TINY_F32), W.make_pool_host(W.TINY_F32)
     assert np.array_equal(p0, p1) and abs(float(p0.std()) - 0.1) < 0.02
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it says so and exits 2
+    before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
