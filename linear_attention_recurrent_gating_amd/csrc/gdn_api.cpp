@@ -166,11 +166,13 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
 // Rows per lane (at most 32, 16 or 8) of the row-split kernel for a config
 // without a block_k override; 0 if no instance fits.  From same-box runs on
 // MI355X (K = V = 128, state streamed from HBM):
-//   * one token: 32, for either storage type and any grid.  Against 8 rows
-//     per lane, fp32 state: bs=32 24.6 vs 27.6 us, bs=64 48.3 vs 50.8 us,
-//     bs=512 351 vs 361 us, the 4/8-head shard at bs=256 49.3 vs 53.5 us;
-//     bf16 state: bs=64 29.2 vs 31.7 us.  Below 16 sequences every choice
-//     takes the same ~14 us;
+//   * one token: 32 from 256 (sequence, k-head) workgroups on, for either
+//     storage type.  Against 8 rows per lane, fp32 state: bs=32 24.6 vs
+//     27.6 us, bs=64 48.3 vs 50.8 us, bs=512 351 vs 361 us, the 4/8-head
+//     shard at bs=256 49.3 vs 53.5 us; bf16 state: bs=64 29.2 vs 31.7 us.
+//     Below 256, 8: each head gets its own 8-wavefront workgroup and the
+//     state streams through twice as many CUs (bs=1 5.8 vs 7.4 us, bs=8 8.3
+//     vs 8.9 us; bf16 state 5.3 vs 7.1 and 6.1 vs 7.6 us);
 //   * token loops: 32 from 512 workgroups on (spec verify 264 vs 300 us with
 //     8; 64 x 16 tokens 102 vs 135 us), and from 256 when intermediate states
 //     are written for 8 or more tokens per sequence (16 x 16 tokens: fp32
@@ -198,7 +200,10 @@ int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool h
         has_inter && c.num_seqs > 0 && c.num_tokens >= 8 * static_cast<int64_t>(c.num_seqs);
     const bool wide = s.multi_token ? (groups >= 512 || (long_inter && groups >= 256)) : true;
     int order[3] = {8, 16, 32};
-    if (kv128 && wide) {
+    if (kv128 && !s.multi_token && groups < 256) {
+        // fewer than 256 (sequence, k-head) pairs: one head per workgroup
+        // and 8 wavefronts each, so the state streams through more CUs
+    } else if (kv128 && wide) {
         order[0] = 32; order[1] = 8; order[2] = 16;
     } else if (!s.multi_token && (!bf16 || (groups < 2048 && K <= 128 && V <= 128))) {
         order[0] = 32; order[1] = 16; order[2] = 8;

@@ -207,17 +207,25 @@ def test_plan_tile_table():
         assert cols.block_v == 64 and cols.waves_per_group == 4   # G * V / 64 tile units
     multi = gdn.gdn_plan(base_cfg(tokens_per_seq=4, num_tokens=16), False)
     assert multi.multi_token == 1
-    # bf16 state: the same 32 rows per lane
-    dec16 = gdn.gdn_plan(base_cfg(state_dtype=gdn.GDN_DTYPE_BF16), False)
+    # bf16 state: the same 32 rows per lane from 256 (sequence, k-head) pairs on
+    dec16 = gdn.gdn_plan(base_cfg(state_dtype=gdn.GDN_DTYPE_BF16, num_seqs=16, num_tokens=16,
+                                  num_k_heads=16, num_v_heads=32, num_slots=16), False)
     assert dec16.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and dec16.block_k == 64   # 32 rows per lane
+    # fewer pairs: 8 rows per lane, one head per 8-wavefront workgroup
+    tiny = gdn.gdn_plan(base_cfg(state_dtype=gdn.GDN_DTYPE_BF16), False)
+    assert tiny.block_k == 16 and tiny.waves_per_group == 8 and tiny.workgroups == 4 * 2 * 2
     # G = 3 (H_k = 2, H_v = 6) with V = 32, BV = 32: 3 wave units per k-head
     odd = gdn.gdn_plan(base_cfg(num_v_heads=6, head_v_dim=32,
                                 kernel_family=gdn.GDN_KERNEL_COLUMN_TILES), True)
     assert odd.waves_per_group == 3 and odd.workgroups == 4 * 2
-    # row split with G = 3, K = V = 128: 2 waves per head, all three heads in a group
+    # row split with G = 3, K = V = 128, a small grid: 8 waves per head, one head per group
     odd_rows = gdn.gdn_plan(base_cfg(num_v_heads=6), False)
-    assert odd_rows.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and odd_rows.block_k == 64
-    assert odd_rows.waves_per_group == 6 and odd_rows.workgroups == 4 * 2
+    assert odd_rows.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and odd_rows.block_k == 16
+    assert odd_rows.waves_per_group == 8 and odd_rows.workgroups == 4 * 2 * 3
+    # a larger grid: 2 waves per head, all three heads in a group
+    odd_big = gdn.gdn_plan(base_cfg(num_v_heads=6, num_seqs=128, num_tokens=128, num_slots=128),
+                           False)
+    assert odd_big.block_k == 64 and odd_big.waves_per_group == 6 and odd_big.workgroups == 128 * 2
     # 16 rows per lane when asked for four waves per workgroup
     odd4 = gdn.gdn_plan(base_cfg(num_v_heads=6, waves_per_group=4), False)
     assert odd4.block_k == 32 and odd4.workgroups == 4 * 2 * 3
