@@ -132,7 +132,8 @@ typedef struct gdn_config {
                                 fits, where block_v is set, and for token
                                 loops without intermediate states at K, V <=
                                 128 other than 128 x 128 from 1024
-                                (sequence, k-head) workgroups); with
+                                (sequence, k-head) workgroups, and for token
+                                loops at 128 x 128 on fewer than 64); with
                                 GDN_LAYOUT_VK,
                                 value rows.  The host sees only the mean
                                 length, so a batch with a few long sequences

@@ -283,6 +283,16 @@ gdn_status row_split_shape(const gdn_config& c, bool has_inter, gdn::LaunchShape
     return finish_shape(s, V);
 }
 
+// Token loops at K = V = 128 on fewer than 64 (sequence, k-head) pairs
+// (one or a few sequences being verified): 16-column tiles in 2-wavefront
+// workgroups spread each head over 8 workgroups, and the dependent token
+// chain runs on narrow tiles (1 x 4 tokens with intermediate states, fp32
+// state: 8.2 vs 11.2 us; 1 x 8: 11.1 vs 16.4 us; bf16 state 8.1 vs 10.5 us).
+bool tiny_token_loop(const gdn_config& c, const gdn::LaunchShape& s) {
+    return s.multi_token && c.head_k_dim == 128 && c.head_v_dim == 128 &&
+           static_cast<int64_t>(c.num_seqs) * c.num_k_heads < 64;
+}
+
 // Column-tile kernel (KV layout, K x block_v tiles per wavefront).
 gdn_status column_tiles_shape(const gdn_config& c, gdn::LaunchShape& s) {
     const int G = c.num_v_heads / c.num_k_heads;
@@ -299,7 +309,8 @@ gdn_status column_tiles_shape(const gdn_config& c, gdn::LaunchShape& s) {
             return fail(GDN_ERR_BAD_ARGUMENT, "no kernel for K = %d with block_v = %d", K,
                         c.block_v);
     }
-    const int bv = c.block_v ? c.block_v : default_block_v(c);
+    const bool tiny = c.block_v == 0 && c.waves_per_group == 0 && tiny_token_loop(c, s);
+    const int bv = c.block_v ? c.block_v : tiny ? 16 : default_block_v(c);
     const int units = G * (V / bv);
     if (c.waves_per_group != 0 && units % c.waves_per_group != 0)
         return fail(GDN_ERR_BAD_ARGUMENT, "waves_per_group = %d must divide G*V/block_v = %d",
@@ -308,7 +319,7 @@ gdn_status column_tiles_shape(const gdn_config& c, gdn::LaunchShape& s) {
     s.block_v = bv;
     s.block_k = K;
     s.rows_rpl_max = 0;
-    s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units);
+    s.waves = c.waves_per_group ? c.waves_per_group : default_waves(units, tiny ? 2 : 8);
     s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
     return finish_shape(s, V);
 }
@@ -320,7 +331,9 @@ gdn_status column_tiles_shape(const gdn_config& c, gdn::LaunchShape& s) {
 // V = 128, 64 x 4 tokens 26.6 vs 31.1 us), within 6% of the best everywhere.
 bool prefer_column_tiles(const gdn_config& c, const gdn::LaunchShape& s, bool has_inter) {
     const int K = c.head_k_dim, V = c.head_v_dim;
-    if (!s.multi_token || has_inter || c.block_k != 0 || c.waves_per_group != 0) return false;
+    if (!s.multi_token || c.block_k != 0 || c.waves_per_group != 0) return false;
+    if (tiny_token_loop(c, s)) return true;
+    if (has_inter) return false;
     if (K > 128 || V > 128 || (K == 128 && V == 128)) return false;
     return static_cast<int64_t>(c.num_seqs) * c.num_k_heads >= 1024;
 }

@@ -343,7 +343,13 @@ def test_plan_chunked():
     # unless intermediate states are written or a tiling override is given
     long = base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096)
     assert gdn.gdn_plan(long, False).kernel_family == gdn.GDN_KERNEL_CHUNKED
-    assert gdn.gdn_plan(long, False, True).kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
+    # with intermediate states on 8 (sequence, k-head) pairs: 16-column tiles
+    tiny_inter = gdn.gdn_plan(long, False, True)
+    assert tiny_inter.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES and tiny_inter.block_v == 16
+    assert tiny_inter.waves_per_group == 2
+    wide_inter = gdn.gdn_plan(base_cfg(tokens_per_seq=64, num_tokens=64 * 64, num_seqs=64,
+                                       num_slots=64, num_k_heads=16, num_v_heads=32), False, True)
+    assert wide_inter.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT
     assert gdn.gdn_plan(base_cfg(tokens_per_seq=4096, num_tokens=4 * 4096, block_v=32),
                         False).kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
     # more (sequence, v-head) workgroups than CUs: from 32 tokens on
