@@ -175,8 +175,9 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
 //     vs 8.9 us; bf16 state 5.3 vs 7.1 and 6.1 vs 7.6 us);
 //   * token loops: 32 from 512 workgroups on (spec verify 264 vs 300 us with
 //     8; 64 x 16 tokens 102 vs 135 us), and from 256 when intermediate states
-//     are written for 8 or more tokens per sequence (16 x 16 tokens: fp32
-//     state 110 vs 119 us, bf16 52 vs 67 us); 8 otherwise (8 long sequences
+//     are written, with fp32 state or for 8 or more tokens per sequence
+//     (16 x 16 tokens: fp32 state 110 vs 119 us, bf16 52 vs 67 us; 24 x 4,
+//     fp32, 53.3 vs 59.7 us); 8 otherwise (8 long sequences
 //     1.67 vs 2.70 ms with 32; 16 x 4 tokens with intermediates, bf16 state,
 //     22.1 vs 22.9 us).
 // Other shapes: one token, 32 with fp32 state (bs=64: K = 64, V = 128 25.8
@@ -197,7 +198,8 @@ int default_rows_per_lane(const gdn_config& c, const gdn::LaunchShape& s, bool h
     const bool bf16 = c.state_dtype == GDN_DTYPE_BF16;
     const int64_t groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads;
     const bool long_inter =
-        has_inter && c.num_seqs > 0 && c.num_tokens >= 8 * static_cast<int64_t>(c.num_seqs);
+        has_inter && c.num_seqs > 0 &&
+        (!bf16 || c.num_tokens >= 8 * static_cast<int64_t>(c.num_seqs));
     const bool wide = s.multi_token ? (groups >= 512 || (long_inter && groups >= 256)) : true;
     int order[3] = {8, 16, 32};
     if (kv128 && !s.multi_token && groups < 256) {

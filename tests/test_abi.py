@@ -261,15 +261,17 @@ def test_plan_row_split_token_loop():
     big = base_cfg(kernel_family=R, tokens_per_seq=4, num_tokens=16, head_k_dim=256, head_v_dim=256)
     assert validate(big) == 7
     # rows per lane of the token loop: 32 from 512 (sequence, k-head) workgroups,
-    # or from 256 when intermediate states are written for >= 8 tokens per
-    # sequence; 8 below
+    # or from 256 when intermediate states are written (with bf16 state: for
+    # >= 8 tokens per sequence); 8 below
     heads = dict(num_k_heads=16, num_v_heads=32)
-    def bk(B, T, inter):
-        cfg = base_cfg(num_seqs=B, tokens_per_seq=T, num_tokens=B * T, num_slots=B, **heads)
+    def bk(B, T, inter, **kw):
+        cfg = base_cfg(num_seqs=B, tokens_per_seq=T, num_tokens=B * T, num_slots=B, **heads, **kw)
         return gdn.gdn_plan(cfg, False, inter).block_k
+    bf16 = dict(state_dtype=gdn.GDN_DTYPE_BF16)
     assert bk(32, 4, False) == 64 and bk(32, 4, True) == 64
-    assert bk(16, 4, False) == 16 and bk(16, 4, True) == 16 and bk(16, 7, True) == 16
-    assert bk(16, 8, True) == 64 and bk(16, 16, True) == 64
+    assert bk(16, 4, False) == 16 and bk(16, 4, True) == 64
+    assert bk(16, 4, True, **bf16) == 16 and bk(16, 7, True, **bf16) == 16
+    assert bk(16, 8, True, **bf16) == 64 and bk(16, 16, True) == 64
     assert bk(8, 16, True) == 16
     # other head dims
     def plan(B, T, inter, K, V, **kw):
