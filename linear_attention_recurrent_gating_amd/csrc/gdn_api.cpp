@@ -135,10 +135,10 @@ gdn_status finish_shape(gdn::LaunchShape& s, int V) {
 
 // Value-row kernel (VK layout): wavefront units per k-head are G v-heads x
 // V/rpw row blocks; the wavefronts never synchronise, so any divisor of the
-// unit count may form a workgroup.  Up to 8 wavefronts with fp32 state, 4
-// with bf16 (MI355X, H 16/32, K = V = 128, bf16 state: bs=512 decode 195.1
-// vs 202.4 us, 256 x 4 tokens 124.5 vs 134.5 us; fp32 state: 372.8 vs 380.5
-// us the other way).
+// unit count may form a workgroup.  Up to 4 wavefronts (MI355X, H 16/32,
+// K = V = 128, bf16 state: bs=512 decode 195.1 vs 202.4 us with 8, 256 x 4
+// tokens 124.5 vs 134.5 us; fp32 state, 8 long sequences 2.23 vs 3.03 ms),
+// except 8 for a single token with fp32 state (bs=512 372.8 vs 380.5 us).
 gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
     const int G = c.num_v_heads / c.num_k_heads;
     const int K = c.head_k_dim, V = c.head_v_dim;
@@ -158,7 +158,8 @@ gdn_status value_rows_shape(const gdn_config& c, gdn::LaunchShape& s) {
     s.block_k = K;
     s.rows_rpl_max = 0;
     s.waves = c.waves_per_group ? c.waves_per_group
-                                : default_waves(units, c.state_dtype == GDN_DTYPE_BF16 ? 4 : 8);
+                                : default_waves(units, c.state_dtype == GDN_DTYPE_BF16 ||
+                                                               s.multi_token ? 4 : 8);
     s.groups = static_cast<int64_t>(c.num_seqs) * c.num_k_heads * (units / s.waves);
     return finish_shape(s, V);
 }
