@@ -39,9 +39,10 @@ CSRC = os.path.join(ROOT, "linear_attention_recurrent_gating_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNEL_NAMES = {1: "gdn_fused_update", 2: "gdn_decode_rows", 3: "gdn_vk_update",
-                4: "gdn_chunk_fwd"}  # by kernel_family
+KERNEL_NAMES = {1: "gdn_fused_update", 2: "gdn_decode_rows", 3: "gdn_vk_decode",
+                4: "gdn_chunk_fwd"}  # by kernel_family (single token for 2 and 3)
 ROW_SPLIT_TOKEN_LOOP = "gdn_rows_tokens"  # family 2 over several tokens per sequence
+VALUE_ROWS_TOKEN_LOOP = "gdn_vk_multi"    # family 3 over several tokens per sequence
 # The sources each kernel is compiled from (the counter profiles are keyed to them).
 _ROWS = ("gdn_rows.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
 KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_device.h", "gdn_internal.h"),
@@ -52,6 +53,8 @@ DEFAULT_SOURCES = ("gdn_kernels.hip", "gdn_tile.h", "gdn_device.h", "gdn_interna
 def kernel_name(info) -> str:
     if info.kernel_family == 2 and info.multi_token:
         return ROW_SPLIT_TOKEN_LOOP
+    if info.kernel_family == 3 and info.multi_token:
+        return VALUE_ROWS_TOKEN_LOOP
     return KERNEL_NAMES[info.kernel_family]
 
 

@@ -137,3 +137,22 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_bench_kernel_names_are_kernel_symbols():
+    """The kernel named in the bench line (and used to find its profiles) is
+    a kernel defined in the HIP sources, for every family and token mode."""
+    import glob
+    import os
+    import re
+    import sys
+    from types import SimpleNamespace
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    src = "".join(open(p).read() for p in
+                  glob.glob(os.path.join(root, "linear_attention_recurrent_gating_amd", "csrc", "*.hip")))
+    for family in (1, 2, 3, 4):
+        for multi in (0, 1):
+            name = bench.kernel_name(SimpleNamespace(kernel_family=family, multi_token=multi))
+            assert re.search(r"__global__[^;{]*\b" + name + r"\s*\(", src), name
