@@ -471,6 +471,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_gb_s": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9,
+                     "traffic_frac": None if traffic is None
+                                     else traffic / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "algorithmic_bytes": alg_bytes, "kernel": kernel_name(info)},
         "cpu_baseline": None,
     }
