@@ -79,3 +79,27 @@ def test_extreme_gates_and_zero_vectors(dev, name, wl, family):
     assert rel_err(after[inp.state_idx[lv]], s_ref[lv]) <= TOL_STATE_GUARD, "state"
     if wl.intermediates:
         assert rel_err(inter.cpu().numpy()[live], i_ref[live]) <= TOL_STATE_GUARD, "inter"
+
+
+LONG = [
+    ("row_split", 2), ("column_tiles", 1), ("chunked", 4),
+]
+
+
+@pytest.mark.parametrize("name,family", LONG, ids=[c[0] for c in LONG])
+def test_long_sequences_fp32(dev, name, family):
+    """Sequences of 3000 to 8192 tokens with fp32 activations (and a weakly
+    decaying head, whose state carries far): rounding does not accumulate
+    past the fp32 bar."""
+    import torch
+    announce(f"long fp32 {name}")
+    wl = W.Workload(f"long_{name}", 190, 2, 1, 1, 2, 128, 128, W.ACT_F32, 3, 0.05, varlen=True,
+                    len_range=(3000, 8192), decay="weak")
+    inp = W.make_host_inputs(wl)
+    pool_np = W.make_pool_host(wl)
+    pool = torch.from_numpy(pool_np).to(dev)
+    out, _ = run_gpu(inp, pool, dev, kernel_family=family)
+    o_ref, s_ref, _, _ = oracle_on_seqs(inp, pool_np[np.maximum(inp.state_idx, 0)],
+                                        np.arange(wl.num_seqs))
+    assert rel_err(to_np(out), o_ref) <= tol_for(wl), "out"
+    assert rel_err(pool.cpu().numpy()[inp.state_idx], s_ref) <= TOL_STATE_GUARD, "state"
