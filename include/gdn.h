@@ -277,8 +277,10 @@ gdn_status gdn_validate(
 gdn_status gdn_plan(const gdn_config* cfg, int has_cu_seqlens, int has_intermediate_states,
                     gdn_launch_info* info);
 
-/* Static description of a status code (never NULL). */
-const char* gdn_status_string(gdn_status status);
+/* Static description of a status code (never NULL).  Takes any int, so that
+ * a value outside gdn_status (from another ABI version, say) is answered with
+ * "unknown status" rather than read as an enumerator it is not. */
+const char* gdn_status_string(int status);
 
 /* Detail of the last error returned on the calling thread ("" if none). */
 const char* gdn_last_error_message(void);

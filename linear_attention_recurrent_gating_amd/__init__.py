@@ -15,7 +15,9 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "_lib", "libgdn.so")
+# GDN_LIBRARY names another build of the same sources (the tests load a
+# build whose host code is compiled with AddressSanitizer this way).
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "_lib", "libgdn.so")
 
 GDN_OK = 0
 GDN_DTYPE_F32 = 0

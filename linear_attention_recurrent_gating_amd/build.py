@@ -36,30 +36,56 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, extra_device_flags=()) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is
+# compiled as usual).  The library is then loaded into a process that preloads
+# clang's ASan runtime (asan_runtime()); the CPU tests run the host-only ABI
+# tests that way.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """clang's shared ASan runtime, to preload into a process that loads a
+    sanitized build."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise FileNotFoundError("clang's libclang_rt.asan-x86_64.so was not found under /opt/rocm/llvm")
+    return found[-1]
+
+
+def build(verbose: bool = False, extra_device_flags=(), out: str = LIB, sanitize: bool = False) -> str:
+    """Compiles libgdn to `out`.  sanitize=True instruments the host code
+    (argument checks, planning, launches) with ASan and UBSan; such a build
+    is for tests only and skips the C example."""
+    libdir = os.path.dirname(os.path.abspath(out))
+    os.makedirs(libdir, exist_ok=True)
+    extra = HOST_SANITIZE if sanitize else []
+    tag = ".san" if sanitize else ""
     cmds, objs = [], []
     for src in DEVICE_SOURCES:
-        obj = os.path.join(LIBDIR, src + ".o")
-        cmds.append([HIPCC, *COMMON, *DEVICE, *extra_device_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(libdir, src + tag + ".o")
+        cmds.append([HIPCC, *COMMON, *DEVICE, *extra_device_flags, *extra, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HOST_SOURCES:
-        obj = os.path.join(LIBDIR, src + ".o")
-        cmds.append([HIPCC, *COMMON, "-I", ROCM_INCLUDE, "-D__HIP_PLATFORM_AMD__", "-x", "c++", "-c",
-                     os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(libdir, src + tag + ".o")
+        cmds.append([HIPCC, *COMMON, "-I", ROCM_INCLUDE, "-D__HIP_PLATFORM_AMD__", "-x", "c++", *extra,
+                     "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     # one compiler process per source, at most MAX_JOBS (default 4) at a time
     jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "4"))))
     with ThreadPoolExecutor(jobs) as pool:
         for f in [pool.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     for o in objs:
         os.remove(o)
-    build_c_example(verbose)
-    return LIB
+    if not sanitize:
+        build_c_example(verbose)
+    return out
 
 
 def c_example_command(out: str = C_EXAMPLE, syntax_only: bool = False):

@@ -66,7 +66,8 @@ gdn_status chunked_shape(const gdn_config& c, gdn::LaunchShape& s) {
     const int64_t rows[] = {c.q_stride_tok ? c.q_stride_tok : int64_t(c.num_k_heads) * K,
                             c.k_stride_tok ? c.k_stride_tok : int64_t(c.num_k_heads) * K,
                             c.v_stride_tok ? c.v_stride_tok : int64_t(c.num_v_heads) * V,
-                            int64_t(c.num_v_heads) * V};
+                            int64_t(c.num_v_heads) * V,
+                            c.ab_stride_tok ? c.ab_stride_tok : int64_t(c.num_v_heads)};
     for (int64_t r : rows)
         if (r * esize * gdn::kChunkedTokens >= (int64_t(1) << 31))
             return fail(GDN_ERR_UNSUPPORTED_SHAPE, "64 token rows of %lld elements exceed 2 GiB",
@@ -110,14 +111,19 @@ int64_t chunked_min_mean_tokens(const gdn_config& c, int64_t base) {
     return static_cast<int64_t>(std::ceil(base * std::sqrt(128.0 * 128.0 / kv)));
 }
 
-bool auto_chunked(const gdn_config& c, bool has_inter) {
+bool auto_chunked(const gdn_config& c, bool has_cu, bool has_inter) {
     if (c.kernel_family != GDN_KERNEL_AUTO || has_inter) return false;
     if (c.block_v != 0 || c.block_k != 0 || c.waves_per_group != 0) return false;
     if (c.num_seqs <= 0) return false;
+    // the tokens the call processes: without cu_seqlens the rows past
+    // num_seqs * tokens_per_seq are not part of any sequence
+    const int64_t tokens = has_cu ? c.num_tokens
+                                  : static_cast<int64_t>(c.num_seqs) * c.tokens_per_seq;
+    if (!has_cu && c.tokens_per_seq <= 1) return false;   // single-token decode
     const bool one_wave = static_cast<int64_t>(c.num_seqs) * c.num_v_heads <= kComputeUnits;
     const int64_t min_mean = chunked_min_mean_tokens(
         c, one_wave ? kChunkedMinMeanTokensOneWave : kChunkedMinMeanTokens);
-    if (c.num_tokens < min_mean * c.num_seqs) return false;
+    if (tokens < min_mean * c.num_seqs) return false;
     gdn::LaunchShape probe{};
     const bool ok = chunked_shape(c, probe) == GDN_OK;
     g_last_error[0] = '\0';
@@ -365,7 +371,7 @@ gdn_status plan_launch(const gdn_config& c, bool has_cu, bool has_inter, gdn::La
         return fail(GDN_ERR_BAD_ARGUMENT, "state_layout = %d is neither GDN_LAYOUT_KV nor _VK",
                     c.state_layout);
 
-    if (c.kernel_family == GDN_KERNEL_CHUNKED || auto_chunked(c, has_inter))
+    if (c.kernel_family == GDN_KERNEL_CHUNKED || auto_chunked(c, has_cu, has_inter))
         return chunked_shape(c, s);
     if (c.state_layout == GDN_LAYOUT_VK)
         return value_rows_shape(c, s);
@@ -718,7 +724,7 @@ gdn_status gdn_gating(const void* a, const void* b, const float* A_log, const fl
     return GDN_OK;
 }
 
-const char* gdn_status_string(gdn_status status) {
+const char* gdn_status_string(int status) {
     switch (status) {
         case GDN_OK: return "ok";
         case GDN_ERR_NULL_POINTER: return "a required pointer is NULL";

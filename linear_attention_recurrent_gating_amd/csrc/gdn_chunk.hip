@@ -20,7 +20,7 @@
 //
 // Design.
 //   * One workgroup walks every chunk of one (sequence, v-head).  Each wave
-//     owns 32 value columns, and their K x 32 slice of the state stays in MFMA
+//     owns 16 value columns, and their K x 16 slice of the state stays in MFMA
 //     accumulators from the first chunk to the last.  There is no chunk index
 //     table and no state round trip through HBM between chunks.
 //   * Everything that depends on the state is a product in which this wave's
@@ -37,10 +37,10 @@
 //     (I + L)^-1, fp32 inputs) is split into hi + lo bf16 parts, and three
 //     products (hi*hi, hi*lo, lo*hi) keep about 16 significant bits of each
 //     term.
-//   * (I + L)^-1 is formed blockwise in fp32.  The 16 x 16 diagonal blocks
-//     use forward substitution on 16 lanes.  The 32 x 32 and 64 x 64 merges
-//     use v_mfma_f32_16x16x4_f32.
-//   * Four workgroup barriers per chunk.  The per-token scalars are double
+//   * Only the 16 x 16 diagonal blocks of (I + L)^-1 are formed (forward
+//     substitution on 16 lanes, fp32); U follows by block forward
+//     substitution with them.
+//   * Two workgroup barriers per chunk.  The per-token scalars are double
 //     buffered, so the next chunk's loads do not wait for the last products.
 
 #include "gdn_device.h"

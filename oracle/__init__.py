@@ -21,17 +21,32 @@ _LIB = os.path.join(_HERE, "libgdn_oracle.so")
 _libs = {}
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+def build(force: bool = True, src: str = _SRC, out: str = _LIB, sanitize: bool = False) -> str:
     """Compile the oracle with gcc (OpenMP across independent units only;
     no fused multiply-add contraction, so each step rounds as written).
-    ``src``/``out`` let tests compile deliberately broken copies."""
+    ``src``/``out`` let tests compile deliberately broken copies;
+    ``sanitize`` builds it with gcc's AddressSanitizer and
+    UndefinedBehaviorSanitizer (load it into a process that preloads
+    ``sanitizer_runtime()``)."""
     if force or not os.path.exists(out):
         tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
                "-ffp-contract=off", "-fno-fast-math", src, "-o", tmp, "-lm"]
+        if sanitize:
+            cmd[1:2] = ["-O1", "-g", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all",
+                        "-fsanitize=address,undefined"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
+
+
+def sanitizer_runtime() -> str:
+    """gcc's ASan runtime (to preload)."""
+    r = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                       check=True).stdout.strip()
+    if not os.path.isabs(r):
+        raise FileNotFoundError("gcc's libasan.so was not found")
+    return r
 
 
 def _load(path: str = _LIB):

@@ -460,8 +460,53 @@ def pin_bf16_state_storage(upd):
     _close(out[1, 0], [0.175, 0.02], 1e-13, "bf16 storage leaves the outputs in double")
 
 
+# (value written to the state, bf16 bit pattern it must be stored as), derived
+# by hand from round-to-nearest-even with 8 significant bits, the subnormal
+# quantum 2^-133 below 2^-126 and overflow to infinity from the midpoint
+# between the largest finite bf16 (2 - 2^-7) 2^127 and 2^128 on.
+BF16_ROUNDING_EDGES = [
+    (3 * 2.0 ** -135, 0x0001),                  # 0.75 quantum rounds up to the smallest subnormal
+    (2.0 ** -134, 0x0000),                      # half a quantum: tie to even (zero)
+    (3 * 2.0 ** -134, 0x0002),                  # 1.5 quanta: tie to even (2)
+    (-5 * 2.0 ** -134, 0x8002),                 # -2.5 quanta: tie to even, sign kept
+    (2.0 ** -126 - 2.0 ** -133, 0x007F),        # largest subnormal, exact
+    (2.0 ** -126 - 2.0 ** -134, 0x0080),        # 127.5 quanta: tie to even = smallest normal
+    (-2.0 ** -150, 0x8000),                     # rounds to zero and keeps the sign
+    (1.0 + 2.0 ** -8, 0x3F80),                  # tie between 1 and 1 + 2^-7: even is 1
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),              # tie between 1 + 2^-7 and 1 + 2^-6: even is the latter
+    (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),     # just above the tie (a float detour would lose it)
+    ((2.0 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),   # largest finite bf16, exact
+    (2.0 ** 128 - 2.0 ** 119 - 2.0 ** 90, 0x7F7F),  # just below the overflow midpoint
+    (2.0 ** 128 - 2.0 ** 119, 0x7F80),          # the midpoint: tie to even overflows to +inf
+    (-1e300, 0xFF80),                           # far beyond the range: -inf
+]
+
+
+def pin_bf16_rounding_edges(upd):
+    """bf16 storage rounds the double-precision state once, to nearest even,
+    through the subnormal range and into overflow.  K = 1, a unit key, eps = 0,
+    beta = 1 (b = +1000) and gamma = 1 (A_log = -1000, so e^A_log is 0) from a
+    zero state make the stored state exactly v: S' = 0 + khat (1 (v - 0)) = v.
+    Each v is then stored as the hand-derived bit pattern above, in the pool
+    and in the intermediate state alike."""
+    vals = np.array([x for x, _ in BF16_ROUNDING_EDGES], np.float64)
+    want = np.array([b for _, b in BF16_ROUNDING_EDGES], np.uint16)
+    n = vals.size
+    one = np.ones((1, 1, 1))
+    pool = np.zeros((1, 1, 1, n), np.uint16)   # bf16 zeros
+    out, inter = upd(one, one, vals.reshape(1, 1, n), np.zeros((1, 1)), np.full((1, 1), 1000.0),
+                     np.full(1, -1000.0), np.zeros(1), pool, np.array([0], np.int32), None,
+                     tokens_per_seq=1, scale=1.0, eps=0.0, intermediates=True)
+    got = pool[0, 0, 0]
+    bad = [f"{vals[i]!r} -> {got[i]:#06x}, want {want[i]:#06x}" for i in range(n) if got[i] != want[i]]
+    assert not bad, "bf16 rounding: " + "; ".join(bad)
+    assert np.array_equal(inter[0, 0, 0], want), "bf16 rounding of the intermediate state"
+    assert np.array_equal(out[0, 0], vals), "the output stays in double (q = k, o = S^T qhat = v)"
+
+
 ALL_PINS = [pin_worked_example, pin_gamma_closed_form, pin_beta_closed_form,
             pin_unit_write, pin_write_and_orthogonal_complement,
             pin_zero_state_output, pin_eps_inside_root, pin_matrix_form,
             pin_chain, pin_gqa_is_mha, pin_scale_invariance, pin_structure,
-            pin_state_layouts, pin_gating_step, pin_bf16_state_storage]
+            pin_state_layouts, pin_gating_step, pin_bf16_state_storage,
+            pin_bf16_rounding_edges]

@@ -387,6 +387,32 @@ def test_plan_chunked():
     assert huge.kernel_family == gdn.GDN_KERNEL_COLUMN_TILES
 
 
+def test_auto_counts_processed_tokens():
+    """Without cu_seqlens only num_seqs * tokens_per_seq rows belong to
+    sequences: a one-token decode over a larger token buffer stays on the
+    single-token row split, and the chunked threshold counts the processed
+    tokens, not the buffer's rows."""
+    dec = gdn.gdn_plan(base_cfg(num_seqs=8, tokens_per_seq=1, num_tokens=512, num_slots=8), False)
+    assert dec.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and dec.multi_token == 0
+    few = gdn.gdn_plan(base_cfg(num_seqs=8, tokens_per_seq=4, num_tokens=4096, num_slots=8,
+                                num_k_heads=16, num_v_heads=32), False)
+    assert few.kernel_family == gdn.GDN_KERNEL_ROW_SPLIT and few.multi_token == 1
+
+
+def test_chunked_ab_stride_offsets():
+    """The chunked kernel addresses 64 token rows of a and b with 32-bit
+    offsets: an a/b token stride whose 64 rows span 2 GiB or more is
+    rejected for the chunked family, and AUTO falls back to a per-token
+    kernel (64-bit row addressing) without an error."""
+    chunked = dict(kernel_family=gdn.GDN_KERNEL_CHUNKED, tokens_per_seq=100, num_tokens=400)
+    big = (1 << 26) + 5          # bf16: 64 rows of it span just over 8 GiB
+    assert validate(base_cfg(ab_stride_tok=big, **chunked)) == 3
+    assert "2 GiB" in gdn.gdn_last_error_message()
+    assert validate(base_cfg(ab_stride_tok=(1 << 23) - 64, **chunked)) == 0   # just under 1 GiB
+    auto = gdn.gdn_plan(base_cfg(ab_stride_tok=big, tokens_per_seq=100, num_tokens=400), False)
+    assert auto.kernel_family != gdn.GDN_KERNEL_CHUNKED and gdn.gdn_last_error_message() == ""
+
+
 def test_chunked_entry_point_validation():
     lib = gdn.raw_library()
     c = base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT)

@@ -7,8 +7,8 @@ bf16 state storage, padding and empty sequences."""
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL_STATE_GUARD, announce, live_rows, oracle_on_seqs, rel_err, to_layout,
-                         to_np, tol_for)
+from gpu_helpers import (TOL_STATE_GUARD, announce, check_vs_oracle, live_rows, oracle_on_seqs,
+                         rel_err, to_layout, to_np, tol_for)
 from linear_attention_recurrent_gating_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -213,8 +213,9 @@ def test_chunked_all_padded(dev):
 @pytest.mark.parametrize("layout", ["KV", "VK"])
 def test_chunked_strided_and_packed_inputs(dev, layout):
     """q/k/v as column slices of one fused projection and a/b packed per
-    k-head ([N, H_k, 2G]: the G b-values, then the G a-values) give the dense
-    chunked result bit for bit."""
+    k-head ([N, H_k, 2G]: the G b-values, then the G a-values; vLLM #37975
+    implementation) match the oracle, and give the dense chunked result bit
+    for bit."""
     import torch
     import linear_attention_recurrent_gating_amd as gdn
     announce(f"chunked strided/packed {layout}")
@@ -242,4 +243,6 @@ def test_chunked_strided_and_packed_inputs(dev, layout):
                                        d["dt_bias"], p_str, d["state_idx"], None, out,
                                        tokens_per_seq=wl.tokens_per_seq, state_layout=layout)
     torch.cuda.synchronize()
+    check_vs_oracle(inp, pool_np, p_str.cpu().numpy(), to_np(out), layout=layout,
+                    what="chunked strided/packed")
     assert torch.equal(out, o_dense) and torch.equal(p_str, p_dense)

@@ -1,0 +1,256 @@
+"""Guard bands around every buffer of a call.
+
+Each tensor the library touches is cut out of a larger allocation.  The
+margins of the inputs (q, k, v, a, b, the gate parameters, the slot indices
+and cu_seqlens) hold NaN or out-of-range sentinels, so a read past a tensor's
+end or before its start poisons the result and fails the oracle comparison.
+The margins of what the library writes (out, intermediate_states, the state
+pool, and g/beta of the gating step) hold a fixed bit pattern that must be
+bit-identical after the call, so a write outside a tensor is caught even when
+it lands in memory nothing else reads.  The slot indices include the first
+and the last slot of the pool, and a sequence with a ragged tail comes last,
+so the final rows of out and of intermediate_states are the ones written at
+the very end of their buffers.  Every kernel family runs: the row split
+(one token and the token loop), the column tiles, the value rows (transposed
+layout) and the chunked forward."""
+import numpy as np
+import pytest
+
+from gpu_helpers import (announce, check_vs_oracle, live_rows, oracle_on_seqs, rel_err,
+                         to_layout, to_np, tol_for)
+from linear_attention_recurrent_gating_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+MARGIN_BYTES = 64 * 1024 + 4096   # more than one 128 x 128 fp32 state tile on each side
+SENTINEL32 = 0x7FA5C3E1           # a NaN with a payload nothing computes
+SENTINEL16 = 0x7FA5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+class Guarded:
+    """A tensor of `shape` placed MARGIN_BYTES into a larger buffer whose
+    margins hold `fill` (a bit pattern for written tensors, a value for read
+    ones)."""
+
+    def __init__(self, shape, dtype, dev, fill_bits=None, fill_value=None):
+        import torch
+        esize = torch.empty(0, dtype=dtype).element_size()
+        self.m = MARGIN_BYTES // esize
+        self.n = int(np.prod(shape)) if len(shape) else 1
+        self.whole = torch.empty(self.n + 2 * self.m, dtype=dtype, device=dev)
+        if fill_bits is not None:
+            ityp = {4: torch.int32, 2: torch.int16}[esize]
+            bits = fill_bits if fill_bits < 2 ** (8 * esize - 1) else fill_bits - 2 ** (8 * esize)
+            self.whole.view(ityp).fill_(bits)
+        else:
+            self.whole.fill_(fill_value)
+        self.t = self.whole[self.m:self.m + self.n].view(shape)
+        self.margins0 = self.margins()
+
+    def margins(self):
+        import torch
+        w = self.whole
+        ityp = {4: torch.int32, 2: torch.int16, 8: torch.int64}[w.element_size()]
+        raw = w.view(ityp)
+        return raw[:self.m].cpu().clone(), raw[self.m + self.n:].cpu().clone()
+
+    def assert_margins_intact(self, what):
+        import torch
+        lo, hi = self.margins()
+        assert torch.equal(lo, self.margins0[0]), f"{what}: the bytes before the tensor changed"
+        assert torch.equal(hi, self.margins0[1]), f"{what}: the bytes after the tensor changed"
+
+
+def guarded_copy(x, dev, fill_value):
+    g = Guarded(tuple(x.shape), x.dtype, dev, fill_value=fill_value)
+    g.t.copy_(x)
+    return g
+
+
+def edge_slots(inp, num_slots, seed):
+    """Live sequences get distinct slots that include 0 and num_slots - 1;
+    padded ones stay -1."""
+    rng = np.random.default_rng(seed)
+    live = np.nonzero(inp.state_idx >= 0)[0]
+    assert len(live) >= 2 and num_slots >= len(live)
+    mid = rng.permutation(np.arange(1, num_slots - 1))[:len(live) - 2]
+    slots = rng.permutation(np.concatenate([[0, num_slots - 1], mid])).astype(np.int32)
+    idx = inp.state_idx.copy()
+    idx[live] = slots
+    inp.state_idx = idx
+    return inp
+
+
+def run_guarded(inp, pool_np, dev, layout="KV", family=0, state_bf16=False, pregated=False,
+                chunked_entry=False, flags=0):
+    """One call with every tensor in a guard band.  Returns (out, inter,
+    pool after) as numpy arrays and checks every margin."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    wl = inp.wl
+    d = W.to_torch(inp, dev)
+    nan = float("nan")
+    gq = guarded_copy(d["q"], dev, nan)
+    gk = guarded_copy(d["k"], dev, nan)
+    gv = guarded_copy(d["v"], dev, nan)
+    ga = guarded_copy(d["a"], dev, nan)
+    gb = guarded_copy(d["b"], dev, nan)
+    gA = guarded_copy(d["A_log"], dev, nan)
+    gdt = guarded_copy(d["dt_bias"], dev, nan)
+    gidx = guarded_copy(d["state_idx"], dev, wl.num_slots + 7)   # out of range if read
+    gcu = None if d["cu_seqlens"] is None else guarded_copy(d["cu_seqlens"], dev, -(1 << 30))
+    act = torch.bfloat16 if wl.act == W.ACT_BF16 else torch.float32
+    N = inp.num_tokens
+    sent = SENTINEL16 if act == torch.bfloat16 else SENTINEL32
+    gout = Guarded((N, wl.num_v_heads, wl.head_v_dim), act, dev, fill_bits=sent)
+    gout.t.fill_(nan)
+    pdtype = torch.bfloat16 if state_bf16 else torch.float32
+    psent = SENTINEL16 if state_bf16 else SENTINEL32
+    gpool = Guarded(tuple(pool_np.shape), pdtype, dev, fill_bits=psent)
+    if state_bf16:
+        gpool.t.view(torch.int16).copy_(torch.from_numpy(pool_np.view(np.int16)))
+    else:
+        gpool.t.copy_(torch.from_numpy(pool_np))
+    ginter = None
+    if wl.intermediates:
+        ginter = Guarded((N, wl.num_v_heads) + tuple(pool_np.shape[2:]), pdtype, dev,
+                         fill_bits=psent)
+        ginter.t.fill_(nan)
+    gated = []
+    cu = None if gcu is None else gcu.t
+    if pregated:
+        gg = Guarded((N, wl.num_v_heads), torch.float32, dev, fill_bits=SENTINEL32)
+        gbeta = Guarded((N, wl.num_v_heads), torch.float32, dev, fill_bits=SENTINEL32)
+        gdn.gdn_gating(ga.t, gb.t, gA.t, gdt.t, gg.t, gbeta.t, num_k_heads=wl.num_k_heads)
+        gated = [(gg, "g"), (gbeta, "beta")]
+        gdn.gdn_recurrent_update(gq.t, gk.t, gv.t, gg.t, gbeta.t, gpool.t, gidx.t, cu, gout.t,
+                                 None if ginter is None else ginter.t,
+                                 tokens_per_seq=wl.tokens_per_seq, kernel_family=family,
+                                 state_layout=layout, flags=flags)
+    elif chunked_entry:
+        gdn.gdn_chunk_gated_delta_rule_fwd(gq.t, gk.t, gv.t, ga.t, gb.t, gA.t, gdt.t, gpool.t,
+                                           gidx.t, cu, gout.t, tokens_per_seq=wl.tokens_per_seq,
+                                           state_layout=layout, flags=flags)
+    else:
+        gdn.gdn_gating_delta_rule_update(gq.t, gk.t, gv.t, ga.t, gb.t, gA.t, gdt.t, gpool.t,
+                                         gidx.t, cu, gout.t, None if ginter is None else ginter.t,
+                                         tokens_per_seq=wl.tokens_per_seq, kernel_family=family,
+                                         state_layout=layout, flags=flags)
+    torch.cuda.synchronize()
+    for g, name in [(gout, "out"), (gpool, "state_pool")] + \
+            ([(ginter, "intermediate_states")] if ginter is not None else []) + gated:
+        g.assert_margins_intact(name)
+    if state_bf16:
+        pool_after = gpool.t.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        pool_after = gpool.t.cpu().numpy()
+    inter = None if ginter is None else ginter.t.cpu().numpy()
+    return to_np(gout.t), inter, pool_after
+
+
+def ragged_last(wl, last_len):
+    """Host inputs whose last sequence has `last_len` tokens (cu_seqlens
+    rebuilt; the token rows are drawn for the new total)."""
+    inp = W.make_host_inputs(wl)
+    lengths = inp.lengths.copy()
+    lengths[-1] = last_len
+    rng = np.random.default_rng(wl.seed + 1000)
+    N = int(lengths.sum())
+    f32 = np.float32
+
+    def draw(shape, std=1.0):
+        x = (std * rng.standard_normal(shape)).astype(f32)
+        if wl.act == W.ACT_BF16:
+            x = W.round_to_bf16(x)[1]
+        return x
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    q = draw((N, wl.num_k_heads, wl.head_k_dim))
+    k = draw((N, wl.num_k_heads, wl.head_k_dim))
+    v = draw((N, wl.num_v_heads, wl.head_v_dim))
+    a = draw((N, wl.num_v_heads))
+    b = draw((N, wl.num_v_heads))
+    bits = {}
+    if wl.act == W.ACT_BF16:
+        bits = {n: W.round_to_bf16(x)[0] for n, x in (("q", q), ("k", k), ("v", v), ("a", a),
+                                                        ("b", b))}
+    return W.HostInputs(wl, q, k, v, a, b, inp.A_log, inp.dt_bias, inp.state_idx, cu, lengths,
+                        bits)
+
+
+CASES = [
+    # (id, workload, ragged last length or None, layout, family, state bf16, pregated, chunked)
+    ("rows_decode", W.Workload("gb_rows_decode", 300, 12, 1, 2, 4, 128, 128, W.ACT_BF16, 16,
+                               0.05, num_padded=2), None, "KV", 2, False, False, False),
+    ("rows_decode_f32_k64", W.Workload("gb_rows_k64", 301, 9, 1, 2, 4, 64, 128, W.ACT_F32, 11,
+                                       0.05, num_padded=1), None, "KV", 2, False, False, False),
+    ("rows_tokens_inter", W.Workload("gb_rows_tok", 302, 7, 1, 2, 4, 128, 128, W.ACT_BF16, 10,
+                                     0.05, varlen=True, len_range=(1, 12), num_padded=1,
+                                     intermediates=True), 7, "KV", 2, False, False, False),
+    ("rows_tokens_bf16_state", W.Workload("gb_rows_bf16s", 303, 6, 1, 2, 4, 128, 128,
+                                          W.ACT_BF16, 9, 0.05, varlen=True, len_range=(1, 9),
+                                          intermediates=True), 5, "KV", 2, True, False, False),
+    ("column_tiles", W.Workload("gb_cols", 304, 6, 1, 2, 4, 128, 128, W.ACT_F32, 9, 0.05,
+                                varlen=True, len_range=(1, 20), num_padded=1,
+                                intermediates=True), 13, "KV", 1, False, False, False),
+    ("value_rows_decode", W.Workload("gb_vk_decode", 305, 10, 1, 2, 4, 128, 128, W.ACT_BF16,
+                                     13, 0.05, num_padded=2), None, "VK", 3, False, False, False),
+    ("value_rows_tokens", W.Workload("gb_vk_tok", 306, 6, 1, 2, 4, 64, 128, W.ACT_BF16, 9, 0.05,
+                                     varlen=True, len_range=(1, 10), intermediates=True), 9,
+     "VK", 3, False, False, False),
+    ("chunked_ragged", W.Workload("gb_chunk", 307, 5, 1, 2, 4, 128, 128, W.ACT_BF16, 8, 0.05,
+                                  varlen=True, len_range=(30, 200), num_padded=1), 131, "KV", 4,
+     False, False, True),
+    ("chunked_f32_vk", W.Workload("gb_chunk_f32", 308, 4, 1, 2, 4, 64, 64, W.ACT_F32, 7, 0.1,
+                                  varlen=True, len_range=(20, 150)), 77, "VK", 4, False, False,
+     True),
+    ("unfused_pair", W.Workload("gb_unfused", 309, 6, 1, 2, 4, 128, 128, W.ACT_BF16, 9, 0.05,
+                                varlen=True, len_range=(1, 6), num_padded=1,
+                                intermediates=True), 3, "KV", 0, False, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_guard_bands(dev, case):
+    name, wl, last_len, layout, family, state_bf16, pregated, chunked = case
+    announce(f"guard bands {name}: {wl.name} layout={layout} family={family} "
+             f"state_bf16={state_bf16} pregated={pregated} chunked={chunked}")
+    inp = ragged_last(wl, last_len) if last_len is not None else W.make_host_inputs(wl)
+    if inp.state_idx[-1] < 0:                     # the last (ragged) sequence must be live
+        idx = inp.state_idx.copy()
+        i = int(np.nonzero(idx >= 0)[0][0])
+        idx[[i, -1]] = idx[[-1, i]]
+        inp.state_idx = idx
+    assert inp.state_idx[-1] >= 0
+    inp = edge_slots(inp, wl.num_slots, wl.seed)
+    pool_f32 = to_layout(W.make_pool_host(wl), layout)
+    if state_bf16:
+        pool_np, _ = W.round_to_bf16(pool_f32)
+    else:
+        pool_np = pool_f32
+    out, inter, pool_after = run_guarded(inp, pool_np, dev, layout=layout, family=family,
+                                         state_bf16=state_bf16, pregated=pregated,
+                                         chunked_entry=chunked)
+    if state_bf16:
+        # bf16 storage: outputs to the activation bar, stored states within
+        # 2^-8 of the oracle's (one rounding), untouched slots bit-identical
+        seqs = np.arange(wl.num_seqs)
+        o_ref, s_ref, _, _ = oracle_on_seqs(inp, pool_np[np.maximum(inp.state_idx, 0)], seqs,
+                                            intermediates=wl.intermediates, layout=layout)
+        live, dead = live_rows(inp)
+        assert rel_err(out[live], o_ref[live]) <= tol_for(wl)
+        assert np.all(np.isnan(out[dead]))
+        lv = inp.state_idx >= 0
+        as_f32 = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)
+        assert rel_err(as_f32(pool_after[inp.state_idx[lv]]), as_f32(s_ref[lv])) <= 2.0 ** -8
+        untouched = np.setdiff1d(np.arange(wl.num_slots), inp.state_idx[lv])
+        assert np.array_equal(pool_after[untouched], pool_np[untouched])
+    else:
+        check_vs_oracle(inp, pool_np, pool_after, out, inter, layout=layout, what=name)

@@ -38,6 +38,13 @@ MUTANTS = {
                                "S[(size_t)kk * V + c] = tile_get(tile, (size_t)kk * V + c, bf16);"),
     "bf16_truncates": ("y = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "y = ldexp(trunc(ldexp(m, 8)), e - 8);"),
     "bf16_one_bit_short": ("y = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "y = ldexp(nearbyint(ldexp(m, 7)), e - 7);"),
+    "bf16_ties_away": ("y = ldexp(nearbyint(ldexp(m, 8)), e - 8);", "y = ldexp(round(ldexp(m, 8)), e - 8);"),
+    "bf16_subnormal_as_normal": ("if (ax < 0x1p-126) {", "if (0) {"),
+    "bf16_subnormal_quantum": ("y = nearbyint(x * 0x1p133) * 0x1p-133;",
+                               "y = nearbyint(x * 0x1p132) * 0x1p-132;"),
+    "bf16_via_float": ("const double m = frexp(x, &e);", "const double m = frexp((double)(float)x, &e);"),
+    "bf16_overflow_saturates": ("const float f = (float)y;",
+                                "const float f = (float)fmax(fmin(y, 0x1.fep127), -0x1.fep127);"),
     "gating_head_index": ("g[e] = -exp(A_log[h]) * oracle_softplus(a[e] + dt_bias[h]);",
                           "g[e] = -exp(A_log[0]) * oracle_softplus(a[e] + dt_bias[h]);"),
     "gating_beta_from_a": ("beta[e] = oracle_sigmoid(b[e]);", "beta[e] = oracle_sigmoid(a[e]);"),

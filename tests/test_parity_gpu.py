@@ -9,8 +9,8 @@ checked over everything."""
 import numpy as np
 import pytest
 
-from gpu_helpers import (TOL_STATE_GUARD, announce, live_rows, oracle_on_seqs, rel_err, run_gpu,
-                         to_layout, to_np, tol_for)
+from gpu_helpers import (TOL_STATE_GUARD, announce, check_vs_oracle, live_rows, oracle_on_seqs,
+                         rel_err, run_gpu, to_layout, to_np, tol_for)
 from linear_attention_recurrent_gating_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -287,30 +287,37 @@ def test_varlen_long_weak_decay(dev, family):
                family=family)
 
 
-@pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
-def test_decode_b512_full_size_sampled(dev, wl):
-    """Full-size decode in the benchmark's launch configuration; the oracle
-    checks 48 sampled sequences (every v-head), the untouched slots are
-    checked bitwise over the whole 4096-slot pool."""
+def check_full_size_decode(wl, dev, layout):
+    """Full-size decode in the benchmark's launch configuration, against the
+    oracle on every sequence: all B x H_v (sequence, v-head) units, every
+    output row and every element of every used state tile.  Untouched slots
+    are checked bitwise over the whole pool."""
     import torch
-    announce(f"{wl.name} full size")
+    announce(f"{wl.name} full size, layout {layout}, all {wl.num_seqs} sequences")
     inp = W.make_host_inputs(wl)
     pool = W.make_pool_torch(wl, dev)
+    if layout == "VK":
+        pool = pool.transpose(-1, -2).contiguous()
     pool0 = pool.clone()
-    out, _ = run_gpu(inp, pool, dev)
-    rng = np.random.default_rng(99)
-    seqs = np.sort(rng.choice(wl.num_seqs, size=48, replace=False))
-    slots = inp.state_idx[seqs]
-    o_ref, s_ref, _, rows = oracle_on_seqs(inp, pool0[torch.from_numpy(slots).long().to(dev)].cpu().numpy(),
-                                           seqs)
-    e_out = rel_err(to_np(out[torch.from_numpy(rows).to(dev)]), o_ref)
+    slots = torch.from_numpy(inp.state_idx).long().to(dev)
+    rows0 = pool0[slots].cpu().numpy()
+    out, _ = run_gpu(inp, pool, dev, layout=layout)
+    seqs = np.arange(wl.num_seqs)
+    o_ref, s_ref, _, rows = oracle_on_seqs(inp, rows0, seqs, layout=layout)
+    assert np.array_equal(rows, np.arange(inp.num_tokens))
+    e_out = rel_err(to_np(out), o_ref)
     assert e_out <= tol_for(wl), f"out error {e_out:.3e}"
-    got = pool[torch.from_numpy(slots).long().to(dev)].cpu().numpy()
-    e_state = rel_err(got, s_ref)
+    e_state = rel_err(pool[slots].cpu().numpy(), s_ref)
     assert e_state <= TOL_STATE_GUARD, f"state error {e_state:.3e}"
     changed = (pool != pool0).flatten(1).any(dim=1).cpu().numpy()
     assert set(np.nonzero(changed)[0]) <= set(inp.state_idx.tolist()), "untouched slot changed"
     assert not torch.isnan(out).any(), "an output row was not written"
+    print(f"{wl.name} {layout}: out {e_out:.2e} state {e_state:.2e} over {wl.num_seqs} sequences")
+
+
+@pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
+def test_decode_b512_full_size(dev, wl):
+    check_full_size_decode(wl, dev, "KV")
 
 
 def test_chain_equals_multi_token_bitwise(dev):
@@ -384,7 +391,8 @@ def test_deterministic(dev):
 
 def test_strided_views_match_dense(dev):
     """q/k/v as column slices of one fused projection (token stride larger
-    than the dense row) give the dense result bit for bit."""
+    than the dense row, vLLM #37975 implementation: views of the fused
+    projection) match the oracle, and give the dense result bit for bit."""
     import torch
     import linear_attention_recurrent_gating_amd as gdn
     announce("strided views")
@@ -406,10 +414,11 @@ def test_strided_views_match_dense(dev):
     v = fused[:, 2 * Hk * K:2 * Hk * K + Hv * V].view(N, Hv, V)
     assert q.stride(0) == width
     p_str = torch.from_numpy(pool_np).to(dev)
-    out = torch.empty(N, Hv, V, dtype=torch.bfloat16, device=dev)
+    out = torch.full((N, Hv, V), float("nan"), dtype=torch.bfloat16, device=dev)
     gdn.gdn_gating_delta_rule_update(q, k, v, d["a"], d["b"], d["A_log"], d["dt_bias"], p_str,
                                      d["state_idx"], None, out, tokens_per_seq=3)
     torch.cuda.synchronize()
+    check_vs_oracle(inp, pool_np, p_str.cpu().numpy(), to_np(out), what="strided q/k/v")
     assert torch.equal(out, o_dense) and torch.equal(p_str, p_dense)
 
 
@@ -518,30 +527,20 @@ def test_vk_workloads(dev, wl):
 
 
 @pytest.mark.parametrize("wl", [W.DECODE_B512, W.DECODE_B512_SHARD], ids=lambda w: w.name)
-def test_vk_decode_b512_full_size_sampled(dev, wl):
-    """Full-size decode with the VK pool, 48 sampled sequences against the
-    oracle, untouched slots bitwise over the whole pool."""
+def test_vk_decode_b512_full_size(dev, wl):
+    """The full-size decode with the VK pool (value-row kernel), every
+    sequence against the oracle."""
     import torch
     import linear_attention_recurrent_gating_amd as gdn
-    announce(f"{wl.name} VK full size")
-    inp = W.make_host_inputs(wl)
-    pool = W.make_pool_torch(wl, dev).transpose(-1, -2).contiguous()
-    pool0 = pool.clone()
-    out, _ = run_gpu(inp, pool, dev, layout="VK")
-    rng = np.random.default_rng(98)
-    seqs = np.sort(rng.choice(wl.num_seqs, size=48, replace=False))
-    sl = torch.from_numpy(inp.state_idx[seqs]).long().to(dev)
-    o_ref, s_ref, _, rows = oracle_on_seqs(inp, pool0[sl].cpu().numpy(), seqs, layout="VK")
-    assert rel_err(to_np(out[torch.from_numpy(rows).to(dev)]), o_ref) <= tol_for(wl)
-    assert rel_err(pool[sl].cpu().numpy(), s_ref) <= TOL_STATE_GUARD
-    changed = (pool != pool0).flatten(1).any(dim=1).cpu().numpy()
-    assert set(np.nonzero(changed)[0]) <= set(inp.state_idx.tolist()), "untouched slot changed"
     B = wl.num_seqs
     info = gdn.gdn_plan(gdn.make_config(torch.empty(B, wl.num_k_heads, 128),
-                                        torch.empty(B, wl.num_v_heads, 128), pool,
-                                        torch.from_numpy(inp.state_idx), state_layout="VK",
+                                        torch.empty(B, wl.num_v_heads, 128),
+                                        torch.empty(1).expand(wl.num_slots, wl.num_v_heads,
+                                                              128, 128),
+                                        torch.zeros(B, dtype=torch.int32), state_layout="VK",
                                         tokens_per_seq=1), False)
     assert info.kernel_family == gdn.GDN_KERNEL_VALUE_ROWS
+    check_full_size_decode(wl, dev, "VK")
 
 
 def test_vk_chain_bitwise(dev):
@@ -626,7 +625,8 @@ UNFUSED_CASES = [
 
 @pytest.mark.parametrize("layout,wl", UNFUSED_CASES, ids=lambda x: x if isinstance(x, str) else x.name)
 def test_unfused_pair_equals_fused(dev, layout, wl):
-    """gdn_gating followed by gdn_recurrent_update gives the fused call's
+    """gdn_gating followed by gdn_recurrent_update (the per-token kernels on
+    precomputed g and beta) matches the oracle, and gives the fused call's
     results bit for bit (gamma = exp of the same fp32 g)."""
     import torch
     import linear_attention_recurrent_gating_amd as gdn
@@ -645,6 +645,9 @@ def test_unfused_pair_equals_fused(dev, layout, wl):
                              d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
                              state_layout=layout)
     torch.cuda.synchronize()
+    check_vs_oracle(inp, pool_np, p_pair.cpu().numpy(), to_np(out),
+                    None if inter is None else inter.cpu().numpy(), layout=layout,
+                    what="unfused pair")
     assert torch.equal(out.nan_to_num(), o_fused.nan_to_num())
     assert torch.equal(p_pair, p_fused)
     if inter is not None:
@@ -655,8 +658,10 @@ def test_unfused_pair_equals_fused(dev, layout, wl):
 @pytest.mark.parametrize("layout", ["KV", "VK"])
 def test_packed_mixed_ba(dev, layout):
     """a and b read straight out of a projection packed per k-head as
-    [N, H_k, 2G] (the G b-values, then the G a-values of the group) give the
-    dense result bit for bit, for the fused call and for the gating step."""
+    [N, H_k, 2G] (the G b-values, then the G a-values of the group; vLLM
+    #37975 implementation) match the oracle on the dense a/b values, and give
+    the dense result bit for bit, for the fused call and for the gating step."""
+    import oracle
     import torch
     import linear_attention_recurrent_gating_amd as gdn
     announce(f"packed mixed_ba {layout}")
@@ -672,15 +677,19 @@ def test_packed_mixed_ba(dev, layout):
     mixed[:, :, G:] = d["a"].view(N, Hk, G)
     b_view, a_view = mixed[:, :, :G], mixed[:, :, G:]
     p_packed = torch.from_numpy(pool_np).to(dev)
-    out = torch.empty_like(o_dense)
+    out = torch.full_like(o_dense, float("nan"))
     gdn.gdn_gating_delta_rule_update(d["q"], d["k"], d["v"], a_view, b_view, d["A_log"],
                                      d["dt_bias"], p_packed, d["state_idx"], None, out,
                                      tokens_per_seq=wl.tokens_per_seq, state_layout=layout)
     torch.cuda.synchronize()
+    check_vs_oracle(inp, pool_np, p_packed.cpu().numpy(), to_np(out), layout=layout,
+                    what="packed a/b")
     assert torch.equal(out, o_dense) and torch.equal(p_packed, p_dense)
     g1, b1 = gdn.gdn_gating(d["a"], d["b"], d["A_log"], d["dt_bias"], num_k_heads=Hk)
     g2, b2 = gdn.gdn_gating(a_view, b_view, d["A_log"], d["dt_bias"])
     torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gating(inp.a, inp.b, inp.A_log, inp.dt_bias)
+    assert rel_err(g2.cpu().numpy(), g_ref) <= 1e-5 and rel_err(b2.cpu().numpy(), b_ref) <= 1e-5
     assert torch.equal(g1, g2) and torch.equal(b1, b2)
 
 
