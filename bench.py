@@ -45,7 +45,8 @@ ROW_SPLIT_TOKEN_LOOP = "gdn_rows_tokens"  # family 2 over several tokens per seq
 VALUE_ROWS_TOKEN_LOOP = "gdn_vk_multi"    # family 3 over several tokens per sequence
 # The sources each kernel is compiled from (the counter profiles are keyed to them).
 _ROWS = ("gdn_rows.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
-KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_device.h", "gdn_internal.h"),
+KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_chunk_common.h", "gdn_device.h",
+                                    "gdn_internal.h"),
                   "gdn_decode_rows": _ROWS, ROW_SPLIT_TOKEN_LOOP: _ROWS}
 DEFAULT_SOURCES = ("gdn_kernels.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
 
@@ -72,14 +73,20 @@ def kernel_source_hash(kernel: str = "gdn_decode_rows") -> str:
     return h.hexdigest()[:16]
 
 
-def profile_path(kernel: str, workload: str, kind: str) -> str:
-    return os.path.join(PROFILES, f"{kernel}__{workload}__{kind}.txt")
+def profile_path(kernel: str, workload: str, kind: str, variant: str = "") -> str:
+    tag = f"__{variant}" if variant else ""
+    return os.path.join(PROFILES, f"{kernel}__{workload}{tag}__{kind}.txt")
 
 
-def counter_traffic(kernel: str, workload: str):
+def profile_variant(state_dtype: str) -> str:
+    """Profiles of runs with bf16 state storage carry their own file names."""
+    return "state_bf16" if state_dtype == "bf16" else ""
+
+
+def counter_traffic(kernel: str, workload: str, variant: str = ""):
     """Counter-measured HBM bytes per launch from the committed profile, or
     None when there is none or the kernel source changed since."""
-    path = profile_path(kernel, workload, "counters")
+    path = profile_path(kernel, workload, "counters", variant)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -147,7 +154,8 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
-def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict):
+def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict,
+                       state_dtype: str = "f32"):
     """Writes the committed text summaries of one workload from rocprofv3 CSV
     output: the --kernel-trace --stats table, and HBM traffic per launch from
     the FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same counter
@@ -182,7 +190,8 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
         lines.append(f"# {kernel} dispatch fields: VGPR_Count {v} (= {2 * int(v)} VGPRs allocated), "
                      f"Accum_VGPR_Count {a}, SGPR_Count {sg}, Scratch_Size {scr}, "
                      f"LDS_Block_Size {lds}, Workgroup_Size {wg}, Grid_Size {grid}")
-    with open(profile_path(kernel, workload, "kernel_trace"), "w") as f:
+    variant = profile_variant(state_dtype)
+    with open(profile_path(kernel, workload, "kernel_trace", variant), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     def per_dispatch(counter, copy):
@@ -201,7 +210,7 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
     f_fac, w_fac = gib_kib / cfetch, gib_kib / cwrite
     traffic = (fetch * f_fac + write * w_fac) * 1024
     wl = W.ALL[workload]
-    alg = W.algorithmic_bytes(W.make_host_inputs(wl))
+    alg = W.algorithmic_bytes(W.make_host_inputs(wl), state_bytes=2 if state_dtype == "bf16" else 4)
     out = [f"# rocprofv3 HBM counters: {kernel}, workload {workload}",
            f"# command (FETCH_SIZE): {commands['fetch']}",
            f"# command (WRITE_SIZE): {commands['write']}",
@@ -217,12 +226,13 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
            f"traffic_bytes_per_launch = {traffic:.0f}",
            f"algorithmic_bytes_per_launch = {alg}",
            f"traffic_over_algorithmic = {traffic / alg:.4f}"]
-    with open(profile_path(kernel, workload, "counters"), "w") as f:
+    with open(profile_path(kernel, workload, "counters", variant), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(lines + out))
 
 
-def summarize_utilization(prof_dir: str, workload: str, kernel: str, run: str):
+def summarize_utilization(prof_dir: str, workload: str, kernel: str, run: str,
+                          state_dtype: str = "f32"):
     """Writes profiles/<kernel>__<workload>__utilization.txt: the mean per
     dispatch of every counter found in the rocprofv3 --pmc passes under
     prof_dir (one subdirectory per pass)."""
@@ -243,7 +253,119 @@ def summarize_utilization(prof_dir: str, workload: str, kernel: str, run: str):
              f"# kernel source sha256[:16] = {kernel_source_hash(kernel)}",
              "# counter = mean over dispatches (dispatches)"]
     lines += [f"{k} = {np.mean(v):.3f}   ({len(v)})" for k, v in sorted(vals.items())]
-    with open(profile_path(kernel, workload, "utilization"), "w") as f:
+    with open(profile_path(kernel, workload, "utilization", profile_variant(state_dtype)), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# (probe kind, workload whose state traffic it mirrors): the in-place
+# read-modify-write stream of each decode shape, the spec-verify pattern
+# (read once, four intermediate tiles and the final state written), and the
+# read-only, write-only and copy streams at the bs=512 shape.  Kinds as in
+# gdn_stream_probe_launch: 0 read, 1 write, 2 in place, 3 copy, 4 spec.
+STREAM_CASES = [(0, "decode_b512_hk16_hv32"), (1, "decode_b512_hk16_hv32"),
+                (2, "decode_b512_hk16_hv32"), (3, "decode_b512_hk16_hv32"),
+                (2, "decode_b512_hk4_hv8"), (2, "qwen3next_decode_b64"),
+                (4, "spec_verify_b128_t4")]
+STREAM_KIND_NAMES = {0: "read only", 1: "write only", 2: "in-place read-modify-write",
+                     3: "copy", 4: "spec-verify pattern (1 read, 4 + 1 writes)"}
+STREAM_TRAFFIC = {0: 1, 1: 1, 2: 2, 3: 2, 4: 6}   # tile-sized transfers per tile
+
+
+def stream_ceiling(args):
+    """Times the memory streams of gdn_stream_probe (the update kernels' state
+    accesses with no arithmetic): every case over the same pool geometry and
+    the same rotated random slot sets as the benchmark, so that each kernel's
+    rate can be put next to its own stream's.  Prints one JSON line."""
+    import ctypes
+    import torch
+    from linear_attention_recurrent_gating_amd import build as libbuild
+    if not os.path.exists(libbuild.PROBE_LIB):
+        raise ImportError(f"{libbuild.PROBE_LIB} is not built")
+    lib = ctypes.CDLL(libbuild.PROBE_LIB)
+    fn = lib.gdn_stream_probe_launch
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    tile_elems = 128 * 128
+    pool_tiles = max(W.ALL[w].num_slots * W.ALL[w].num_v_heads for _, w in STREAM_CASES)
+    pool = torch.zeros(pool_tiles * tile_elems, dtype=torch.float32, device=dev)
+    dst = torch.zeros(pool_tiles * tile_elems, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    results = []
+    for kind, wname in STREAM_CASES:
+        wl = W.ALL[wname]
+        inp = W.make_host_inputs(wl)
+        live = int((inp.state_idx >= 0).sum())
+        tiles_per_launch = live * wl.num_v_heads
+        sets = max(1, min(args.slot_sets, wl.num_slots // live))
+        rng = np.random.default_rng(wl.seed + 7)
+        perm = rng.permutation(wl.num_slots)
+        idx_sets = []
+        for s_ in range(sets):
+            slots = perm[s_ * live:(s_ + 1) * live]
+            t = (slots[:, None] * wl.num_v_heads + np.arange(wl.num_v_heads)[None, :]).reshape(-1)
+            assert t.max() < pool_tiles
+            idx_sets.append(torch.from_numpy(t.astype(np.int32)).to(dev))
+        assert kind != 4 or 4 * tiles_per_launch <= pool_tiles
+        sink = torch.zeros(128 * tiles_per_launch, dtype=torch.float32, device=dev)
+
+        def launch(i):
+            rc = fn(kind, pool.data_ptr(), dst.data_ptr(), idx_sets[i % sets].data_ptr(),
+                    tiles_per_launch, sink.data_ptr(), 1.0, wl.num_v_heads,
+                    ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        for i in range(args.warmup):
+            launch(i)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            launch(args.warmup + i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / args.steps * 1e3
+        nbytes = STREAM_TRAFFIC[kind] * tiles_per_launch * tile_elems * 4
+        results.append({"kind": kind, "stream": STREAM_KIND_NAMES[kind], "workload": wname,
+                        "tiles_per_launch": tiles_per_launch, "grid": tiles_per_launch // 2,
+                        "bytes_per_launch": nbytes, "us_per_launch": us,
+                        "gb_s": nbytes / (us * 1e-6) / 1e9,
+                        "frac_of_8tb_s": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+        print(f"# {STREAM_KIND_NAMES[kind]:45s} {wname:24s} {tiles_per_launch:6d} tiles "
+              f"{us:8.1f} us {results[-1]['gb_s']:8.1f} GB/s", flush=True)
+    print(json.dumps({"stream_ceiling": results, "steps": args.steps, "warmup": args.warmup,
+                      "slot_sets": args.slot_sets}), flush=True)
+
+
+def summarize_stream(prof_dir: str, command: str):
+    """Writes profiles/stream_ceiling__decode_state_tiles.txt from a rocprofv3
+    --kernel-trace of `bench.py --stream-ceiling`: per probe kind and grid
+    size (one per case), the mean dispatch duration and the rate it gives."""
+    import re
+    recs = _csv_rows(os.path.join(prof_dir, "run_kernel_trace.csv"))
+    groups = {}
+    for r in recs:
+        m = re.search(r"gdn_stream_probe<(\d)>", r["Kernel_Name"])
+        if not m:
+            continue
+        key = (int(m.group(1)), int(r["Grid_Size_X"]) // 256)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# rocprofv3 kernel trace of the memory-stream probes (gdn_stream_probe<kind>,",
+             "# csrc/stream_probe.hip): the update kernels' state accesses with no arithmetic,",
+             "# 64 KiB fp32 tiles at the random slots of the benchmark's rotated slot sets.",
+             f"# command: {command}",
+             "# kind | stream | workgroups (2 tiles each) | dispatches | mean_us | median_us | "
+             "bytes_per_dispatch | GB/s (mean) | of 8 TB/s"]
+    for (kind, grid), durs in sorted(groups.items()):
+        durs = np.array(durs)
+        nbytes = STREAM_TRAFFIC[kind] * 2 * grid * 128 * 128 * 4
+        gbs = nbytes / (durs.mean() * 1e-6) / 1e9
+        lines.append(f"{kind} | {STREAM_KIND_NAMES[kind]} | {grid} | {durs.size} | {durs.mean():.1f} | "
+                     f"{np.median(durs):.1f} | {nbytes} | {gbs:.1f} | {gbs / HBM_PEAK_GBS:.3f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "stream_ceiling__decode_state_tiles.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -274,6 +396,13 @@ def main():
                     help="time the unfused pair instead: gdn_gating + gdn_recurrent_update per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead: time a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="instead: time the state-tile memory streams with no arithmetic (read, "
+                         "write, in-place read-modify-write, copy, spec-verify pattern) at the "
+                         "decode workloads' shapes")
+    ap.add_argument("--summarize-stream", metavar="DIR",
+                    help="instead: write profiles/stream_ceiling__decode_state_tiles.txt from a "
+                         "rocprofv3 --kernel-trace of --stream-ceiling (CSV files in DIR)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="instead: write profiles/ summaries from rocprofv3 CSV output in DIR "
                          "(subdirectories trace, FETCH_SIZE, WRITE_SIZE, copy_FETCH_SIZE, "
@@ -284,16 +413,23 @@ def main():
     ap.add_argument("--kernel", default="gdn_decode_rows", help="kernel name for --summarize-profiles")
     args = ap.parse_args()
 
+    run = f"python3 bench.py --workload {args.workload}" + (
+        f" --family {args.family}" if args.family else "") + (
+        f" --state-dtype {args.state_dtype}" if args.state_dtype != "f32" else "")
     if args.summarize_utilization:
-        run = f"python3 bench.py --workload {args.workload}" + (
-            f" --family {args.family}" if args.family else "")
-        summarize_utilization(args.summarize_utilization, args.workload, args.kernel, run)
+        summarize_utilization(args.summarize_utilization, args.workload, args.kernel, run,
+                              args.state_dtype)
+        return
+
+    if args.summarize_stream:
+        summarize_stream(args.summarize_stream,
+                         f"rocprofv3 --kernel-trace --output-format csv -d {args.summarize_stream} "
+                         f"-o run -- python3 bench.py --stream-ceiling --steps {args.steps} "
+                         f"--warmup {args.warmup}")
         return
 
     if args.summarize_profiles:
         d = args.summarize_profiles
-        run = f"python3 bench.py --workload {args.workload}" + (
-            f" --family {args.family}" if args.family else "")
         summarize_profiles(d, args.workload, args.kernel, {
             "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
                      f"{run} --steps 50 --warmup 5 --cpu-budget 0",
@@ -304,7 +440,8 @@ def main():
             "copy": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d "
                     f"{d}/copy_<counter> -o run -- python3 bench.py --copy-calibration --steps 3 "
                     f"--warmup 1",
-            "summary": f"{run} --kernel {args.kernel} --summarize-profiles {d}"})
+            "summary": f"{run} --kernel {args.kernel} --summarize-profiles {d}"},
+            args.state_dtype)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -316,6 +453,10 @@ def main():
     import torch
     import linear_attention_recurrent_gating_amd as gdn
     dev = torch.device("cuda:0")
+
+    if args.stream_ceiling:
+        stream_ceiling(args)
+        return
 
     if args.copy_calibration:
         n = 1 << 28  # 1 GiB of fp32
@@ -435,11 +576,13 @@ def main():
                                         state_layout=args.layout),
                         d["cu_seqlens"] is not None, inter is not None)
 
-    # The committed counter profiles were taken with the default options
-    # (fp32 state, KV layout, library tiling, fused gates); other runs get none.
-    profiled = (args.state_dtype == "f32" and args.layout == "KV" and not args.unfused
+    # The committed counter profiles were taken with the library's tiling, the
+    # KV layout and fused gates (fp32 state, or bf16 state under their own
+    # file names); other runs get none.
+    profiled = (args.layout == "KV" and not args.unfused
                 and not (args.block_v or args.block_k or args.waves))
-    traffic = counter_traffic(kernel_name(info), wl.name) if profiled else None
+    traffic = (counter_traffic(kernel_name(info), wl.name, profile_variant(args.state_dtype))
+               if profiled else None)
     res = {
         "metric": METRIC,
         "value": value,

@@ -18,6 +18,9 @@ ROCM_LIB = "/opt/rocm/lib"
 # A plain-C program that drives the C-ABI without Python (built next to the library).
 C_EXAMPLE_SRC = os.path.join(ROOT, "examples", "c_abi_decode.c")
 C_EXAMPLE = os.path.join(LIBDIR, "c_abi_decode")
+# Memory-stream probes the benchmark times next to the update (not part of libgdn).
+PROBE_SRC = os.path.join(CSRC, "stream_probe.hip")
+PROBE_LIB = os.path.join(LIBDIR, "libgdn_stream_probe.so")
 
 DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_rows.hip", "gdn_chunk.hip"]
 HOST_SOURCES = ["gdn_api.cpp"]
@@ -85,7 +88,15 @@ def build(verbose: bool = False, extra_device_flags=(), out: str = LIB, sanitize
         os.remove(o)
     if not sanitize:
         build_c_example(verbose)
+        build_stream_probe(verbose)
     return out
+
+
+def build_stream_probe(verbose: bool = False) -> str:
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *COMMON, *DEVICE, "-shared", PROBE_SRC, "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def c_example_command(out: str = C_EXAMPLE, syntax_only: bool = False):

@@ -1,0 +1,178 @@
+// Matrix-core helpers shared by the chunked forward kernels (gdn_chunk.hip:
+// one workgroup per (sequence, v-head) building every matrix itself;
+// gdn_chunk_ws.hip: a pre-pass over all chunks plus a state pass).  Device
+// code only.
+#pragma once
+
+#include "gdn_device.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;           // tokens per chunk
+
+__device__ __forceinline__ f32x4 mma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x = hi + lo + O(2^-17 |x|), both parts bf16 (round to nearest even).
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: A[m][4 g + i] and B[4 g + i][n] in lane (g, m / n);
+// the accumulator layout of a 16-row tile is exactly its B-operand layout.
+__device__ __forceinline__ f32x4 mma16(const bf16x4& a, const bf16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                      __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+struct Split4 {
+    bf16x4 hi, lo;
+};
+
+__device__ __forceinline__ Split4 split_tile(const f32x4& x) {
+    Split4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split_bf16(x[e], h, l);
+        r.hi[e] = h;
+        r.lo[e] = l;
+    }
+    return r;
+}
+
+// acc += A X for a 16 x 16 block A given as bf16 hi/lo parts (this lane's
+// four elements, read from LDS by the caller ahead of the products) and X a
+// 16-row accumulator tile of this lane split the same way: hi*hi + hi*lo +
+// lo*hi.
+__device__ __forceinline__ f32x4 mma16_split(f32x4 acc, const bf16x4& ah, const bf16x4& al,
+                                             const Split4& x) {
+    acc = mma16(ah, x.hi, acc);
+    acc = mma16(ah, x.lo, acc);
+    acc = mma16(al, x.hi, acc);
+    return acc;
+}
+
+struct Split8 {
+    bf16x8 hi, lo;
+};
+
+// The B operand of one 32-deep step taken from two 16-row accumulator tiles
+// of this lane: element e < 4 is row 4*(lane/16) + e of tile a, element e >= 4
+// row 4*(lane/16) + e - 4 of tile b.
+__device__ __forceinline__ Split8 operand_from_tiles(const f32x4& a, const f32x4& b) {
+    Split8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split_bf16(a[e], h, l);
+        r.hi[e] = h;
+        r.lo[e] = l;
+        split_bf16(b[e], h, l);
+        r.hi[4 + e] = h;
+        r.lo[4 + e] = l;
+    }
+    return r;
+}
+
+// The matching A operand: elements p[0..3] and p[16..19] of an LDS row.
+__device__ __forceinline__ bf16x8 lds_perm8(const __bf16* p) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight consecutive bf16 of an LDS row (16-byte aligned).
+__device__ __forceinline__ bf16x8 lds_row8(const __bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Eight consecutive activation elements at byte offset `off`, widened to fp32.
+template <int ACT>
+__device__ __forceinline__ void buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[8]) {
+    if constexpr (ACT == 0) {
+        const u32x4v a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const u32x4v b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = __uint_as_float(a[e]);
+            x[4 + e] = __uint_as_float(b[e]);
+        }
+    } else {
+        const u32x4v a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16_lo(a[e]);
+            x[2 * e + 1] = bf16_hi(a[e]);
+        }
+    }
+}
+
+// Inclusive prefix sum over the 64 lanes: a Hillis-Steele scan inside each
+// 16-lane row (row_shr 1, 2, 4, 8; lanes shifted in from outside the row add
+// 0), then the row totals carried down with row_bcast:15 and row_bcast:31.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, true));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_or_zero(double v) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(b)), CTRL, ROW_MASK, 0xF, true));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(b >> 32)), CTRL, ROW_MASK, 0xF, true));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// In fp64: the chunk's log-decay prefix sums can reach thousands when a
+// token's gate saturates, and the Gram scaling needs exp(G_t - G_s) for
+// neighbouring tokens, a small difference of two large sums.
+__device__ __forceinline__ double wave_prefix_sum(double x) {
+    x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+    x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+    x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+    x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+    x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), l));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// LDS written by some lanes of this wavefront becomes visible to its others.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Staging loads of one chunk, issued a chunk ahead so that they land while
+// the previous chunk's products run: raw keys and queries (16-byte vectors,
+// NQK per lane) and the raw gate inputs of token `lane` (wave 0).
+template <int ACT, int NQK>
+struct ChunkLoads {
+    static constexpr int VEC = ACT == 0 ? 2 : 1;   // 16-byte vectors per 8 elements
+    u32x4v k[NQK][VEC];
+    u32x4v q[NQK][VEC];
+    float ga, gb;
+};
+
+}  // namespace
+}  // namespace gdn

@@ -151,7 +151,10 @@ def run_guarded(inp, pool_np, dev, layout="KV", family=0, state_bf16=False, preg
         pool_after = gpool.t.view(torch.int16).cpu().numpy().view(np.uint16)
     else:
         pool_after = gpool.t.cpu().numpy()
-    inter = None if ginter is None else ginter.t.cpu().numpy()
+    inter = None
+    if ginter is not None:
+        inter = (ginter.t.view(torch.int16).cpu().numpy().view(np.uint16) if state_bf16
+                 else ginter.t.cpu().numpy())
     return to_np(gout.t), inter, pool_after
 
 
@@ -242,8 +245,8 @@ def test_guard_bands(dev, case):
         # bf16 storage: outputs to the activation bar, stored states within
         # 2^-8 of the oracle's (one rounding), untouched slots bit-identical
         seqs = np.arange(wl.num_seqs)
-        o_ref, s_ref, _, _ = oracle_on_seqs(inp, pool_np[np.maximum(inp.state_idx, 0)], seqs,
-                                            intermediates=wl.intermediates, layout=layout)
+        o_ref, s_ref, i_ref, _ = oracle_on_seqs(inp, pool_np[np.maximum(inp.state_idx, 0)], seqs,
+                                                intermediates=wl.intermediates, layout=layout)
         live, dead = live_rows(inp)
         assert rel_err(out[live], o_ref[live]) <= tol_for(wl)
         assert np.all(np.isnan(out[dead]))
@@ -252,5 +255,10 @@ def test_guard_bands(dev, case):
         assert rel_err(as_f32(pool_after[inp.state_idx[lv]]), as_f32(s_ref[lv])) <= 2.0 ** -8
         untouched = np.setdiff1d(np.arange(wl.num_slots), inp.state_idx[lv])
         assert np.array_equal(pool_after[untouched], pool_np[untouched])
+        if inter is not None:
+            assert rel_err(as_f32(inter[live]), as_f32(i_ref[live])) <= 2.0 ** -8
+            ends = np.cumsum(inp.lengths) - 1
+            for i in np.nonzero(lv)[0]:
+                assert np.array_equal(inter[ends[i]], pool_after[inp.state_idx[i]])
     else:
         check_vs_oracle(inp, pool_np, pool_after, out, inter, layout=layout, what=name)
