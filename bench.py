@@ -45,13 +45,18 @@ ROW_SPLIT_TOKEN_LOOP = "gdn_rows_tokens"  # family 2 over several tokens per seq
 VALUE_ROWS_TOKEN_LOOP = "gdn_vk_multi"    # family 3 over several tokens per sequence
 # The sources each kernel is compiled from (the counter profiles are keyed to them).
 _ROWS = ("gdn_rows.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
+CHUNK_WS_KERNELS = "gdn_chunk_prep+gdn_chunk_state"   # the two-kernel chunked form
 KERNEL_SOURCES = {"gdn_chunk_fwd": ("gdn_chunk.hip", "gdn_chunk_common.h", "gdn_device.h",
                                     "gdn_internal.h"),
+                  CHUNK_WS_KERNELS: ("gdn_chunk_ws.hip", "gdn_chunk_common.h", "gdn_device.h",
+                                     "gdn_internal.h"),
                   "gdn_decode_rows": _ROWS, ROW_SPLIT_TOKEN_LOOP: _ROWS}
 DEFAULT_SOURCES = ("gdn_kernels.hip", "gdn_tile.h", "gdn_device.h", "gdn_internal.h")
 
 
-def kernel_name(info) -> str:
+def kernel_name(info, chunk_workspace: bool = False) -> str:
+    if info.kernel_family == 4 and chunk_workspace:
+        return CHUNK_WS_KERNELS
     if info.kernel_family == 2 and info.multi_token:
         return ROW_SPLIT_TOKEN_LOOP
     if info.kernel_family == 3 and info.multi_token:
@@ -266,10 +271,13 @@ def summarize_utilization(prof_dir: str, workload: str, kernel: str, run: str,
 STREAM_CASES = [(0, "decode_b512_hk16_hv32"), (1, "decode_b512_hk16_hv32"),
                 (2, "decode_b512_hk16_hv32"), (3, "decode_b512_hk16_hv32"),
                 (2, "decode_b512_hk4_hv8"), (2, "qwen3next_decode_b64"),
-                (4, "spec_verify_b128_t4")]
+                (4, "spec_verify_b128_t4"), (5, "decode_b512_hk16_hv32"),
+                (5, "decode_b512_hk4_hv8"), (5, "qwen3next_decode_b64")]
 STREAM_KIND_NAMES = {0: "read only", 1: "write only", 2: "in-place read-modify-write",
-                     3: "copy", 4: "spec-verify pattern (1 read, 4 + 1 writes)"}
-STREAM_TRAFFIC = {0: 1, 1: 1, 2: 2, 3: 2, 4: 6}   # tile-sized transfers per tile
+                     3: "copy", 4: "spec-verify pattern (1 read, 4 + 1 writes)",
+                     5: "in-place read-modify-write, bf16 tiles"}
+STREAM_TRAFFIC = {0: 1, 1: 1, 2: 2, 3: 2, 4: 6, 5: 2}   # tile-sized transfers per tile
+STREAM_TILE_BYTES = {5: 128 * 128 * 2}                  # default: fp32 128 x 128 tiles
 
 
 def stream_ceiling(args):
@@ -327,7 +335,7 @@ def stream_ceiling(args):
         ev1.record(stream)
         torch.cuda.synchronize()
         us = ev0.elapsed_time(ev1) / args.steps * 1e3
-        nbytes = STREAM_TRAFFIC[kind] * tiles_per_launch * tile_elems * 4
+        nbytes = STREAM_TRAFFIC[kind] * tiles_per_launch * STREAM_TILE_BYTES.get(kind, tile_elems * 4)
         results.append({"kind": kind, "stream": STREAM_KIND_NAMES[kind], "workload": wname,
                         "tiles_per_launch": tiles_per_launch, "grid": tiles_per_launch // 2,
                         "bytes_per_launch": nbytes, "us_per_launch": us,
@@ -347,10 +355,10 @@ def summarize_stream(prof_dir: str, command: str):
     recs = _csv_rows(os.path.join(prof_dir, "run_kernel_trace.csv"))
     groups = {}
     for r in recs:
-        m = re.search(r"gdn_stream_probe<(\d)>", r["Kernel_Name"])
+        m = re.search(r"gdn_stream_probe(?:<(\d)>|_bf16)", r["Kernel_Name"])
         if not m:
             continue
-        key = (int(m.group(1)), int(r["Grid_Size_X"]) // 256)
+        key = (int(m.group(1)) if m.group(1) else 5, int(r["Grid_Size_X"]) // 256)
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# rocprofv3 kernel trace of the memory-stream probes (gdn_stream_probe<kind>,",
              "# csrc/stream_probe.hip): the update kernels' state accesses with no arithmetic,",
@@ -360,12 +368,162 @@ def summarize_stream(prof_dir: str, command: str):
              "bytes_per_dispatch | GB/s (mean) | of 8 TB/s"]
     for (kind, grid), durs in sorted(groups.items()):
         durs = np.array(durs)
-        nbytes = STREAM_TRAFFIC[kind] * 2 * grid * 128 * 128 * 4
+        nbytes = STREAM_TRAFFIC[kind] * 2 * grid * STREAM_TILE_BYTES.get(kind, 128 * 128 * 4)
         gbs = nbytes / (durs.mean() * 1e-6) / 1e9
         lines.append(f"{kind} | {STREAM_KIND_NAMES[kind]} | {grid} | {durs.size} | {durs.mean():.1f} | "
                      f"{np.median(durs):.1f} | {nbytes} | {gbs:.1f} | {gbs / HBM_PEAK_GBS:.3f}")
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, "stream_ceiling__decode_state_tiles.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# Shapes of the AUTO sweep: (K, V, B, T, intermediate states, state dtype), all
+# with H_k = 16, H_v = 32 and bf16 activations.
+SWEEP_SHAPES = [(128, 128, B, 1, False, sd) for B in (1, 8, 64, 512) for sd in ("f32", "bf16")] + \
+               [(128, 128, B, T, True, sd) for B, T in ((1, 4), (16, 4), (128, 4), (16, 16))
+                for sd in ("f32", "bf16")] + \
+               [(128, 128, B, T, False, "f32") for B, T in ((64, 4), (64, 16), (8, 64), (64, 64))] + \
+               [(K, V, 64, T, T > 1, "f32") for K, V in ((64, 64), (128, 64), (64, 128), (256, 256))
+                for T in (1, 4)]
+
+
+def auto_sweep(args):
+    """Times AUTO's choice against every kernel family and tile that has an
+    instance, over SWEEP_SHAPES, and writes profiles/auto_table__sweep.txt.
+    Each candidate runs on rotated disjoint slot sets (the state streamed from
+    HBM); the candidates of a shape are timed twice, in one order and then
+    the reverse, and the faster of the two is kept."""
+    import torch
+    import linear_attention_recurrent_gating_amd as gdn
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    lines = ["# AUTO against every kernel family and tile, MI355X, H_k = 16, H_v = 32, bf16 "
+             "activations; mean kernel us per call from HIP events",
+             f"# command: python3 bench.py --sweep --steps {args.steps} --warmup {args.warmup}",
+             "# K | V | B | T | inter | state | AUTO pick | AUTO us | best candidate | best us | "
+             "AUTO / best"]
+    worst = 1.0
+    for K, V, B, T, inter_on, sd in SWEEP_SHAPES:
+        wl = W.Workload(f"sweep_{K}_{V}_{B}_{T}", 300 + B + T + K, B, T, 16, 32, K, V, W.ACT_BF16,
+                        max(8 * B, 16), 0.05, intermediates=inter_on)
+        inp = W.make_host_inputs(wl)
+        d = W.to_torch(inp, dev)
+        pool = torch.randn(wl.num_slots, 32, K, V, device=dev) * 0.05
+        if sd == "bf16":
+            pool = pool.to(torch.bfloat16)
+        sets = max(1, wl.num_slots // B)
+        perm = torch.randperm(wl.num_slots, device=dev).to(torch.int32)
+        idx_sets = [perm[i * B:(i + 1) * B].contiguous() for i in range(sets)]
+        N = inp.num_tokens
+        out = torch.empty(N, 32, V, dtype=torch.bfloat16, device=dev)
+        inter = (torch.empty((N, 32, K, V), dtype=pool.dtype, device=dev) if inter_on else None)
+        cands = [("auto", {})]
+        cands += [(f"rows bk={bk}", {"kernel_family": 2, "block_k": bk}) for bk in (8, 16, 32, 64, 128)]
+        cands += [(f"cols bv={bv}", {"kernel_family": 1, "block_v": bv}) for bv in (16, 32, 64)]
+        if T > 1 and not inter_on:
+            cands.append(("chunked", {"kernel_family": 4}))
+        valid = []
+        for name, kw in cands:
+            cfg = gdn.make_config(d["q"], d["v"], pool, idx_sets[0], None, tokens_per_seq=T, **kw)
+            try:
+                info = gdn.gdn_plan(cfg, False, inter_on)
+            except gdn.GdnError:
+                continue
+            label = name if name != "auto" else \
+                {1: f"cols bv={info.block_v}", 2: f"rows bk={info.block_k}",
+                 4: "chunked"}.get(info.kernel_family, str(info.kernel_family))
+            valid.append((name, kw, label))
+
+        def time_one(kw):
+            def launch(i):
+                gdn.gdn_gating_delta_rule_update(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+                                                 d["dt_bias"], pool, idx_sets[i % sets], None, out,
+                                                 inter, tokens_per_seq=T, **kw)
+            for i in range(args.warmup):
+                launch(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.steps):
+                launch(args.warmup + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps * 1e3
+
+        best = {}
+        for order in (valid, valid[::-1]):
+            for name, kw, _ in order:
+                us = time_one(kw)
+                best[name] = min(best.get(name, float("inf")), us)
+        auto_label = next(lbl for n, _, lbl in valid if n == "auto")
+        others = [(best[n], n) for n, _, _ in valid if n != "auto"]
+        b_us, b_name = min(others)
+        ratio = best["auto"] / b_us
+        worst = max(worst, ratio)
+        lines.append(f"{K} | {V} | {B} | {T} | {int(inter_on)} | {sd} | {auto_label} | "
+                     f"{best['auto']:.1f} | {b_name} | {b_us:.1f} | {ratio:.3f}")
+        print(lines[-1], flush=True)
+        del pool, inter, out
+        torch.cuda.empty_cache()
+    lines.append(f"# largest AUTO / best: {worst:.3f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "auto_table__sweep.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(lines[-1])
+
+
+def summarize_counter_check(root: str):
+    """Writes profiles/hbm_counters__crosscheck.txt: the raw TCC request
+    counters next to FETCH_SIZE / WRITE_SIZE, for the stream probes (whose
+    bytes are exact) and the bs=512 decode.  root holds the rocprofv3 --pmc
+    output directories raw_rd_<run>, raw_wr_<run> and fs_<run> for run in
+    (stream, decode)."""
+    import re
+    runs = {"stream": "python3 bench.py --stream-ceiling --steps 2 --warmup 1",
+            "decode": "python3 bench.py --steps 5 --warmup 1 --cpu-budget 0"}
+    passes = {"raw_rd": "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_BUBBLE_sum TCC_EA0_RDREQ_DRAM_sum",
+              "raw_wr": "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum TCC_EA0_WRREQ_DRAM_sum",
+              "fs": "FETCH_SIZE"}
+    lines = ["# HBM traffic counters cross-checked on gfx950 (rocprofv3 --pmc, mean per dispatch).",
+             "# FETCH_SIZE is (TCC_BUBBLE*128 + (TCC_EA0_RDREQ - TCC_BUBBLE - RDREQ_32B)*64 +",
+             "# RDREQ_32B*32) / 1024 in this ROCm's counter table, TCC_BUBBLE being the 128-byte",
+             "# read requests.  On these kernels TCC_BUBBLE and RDREQ_32B read 0 while every",
+             "# read request is 128 bytes (RDREQ x 128 = the bytes a probe reads), so FETCH_SIZE",
+             "# reports half the bytes read; WRITE_SIZE (64-byte write requests x 64) is exact."]
+    for run, cmd in runs.items():
+        for ps, counters in passes.items():
+            lines.append(f"# command: rocprofv3 --pmc {counters} --output-format csv -d "
+                         f"{root}/{ps}_{run} -o run -- {cmd}")
+    lines.append("# kernel | grid | bytes read (exact, probes) | RDREQ | RDREQ x 128 | BUBBLE | "
+                 "RDREQ_32B | FETCH_SIZE KiB x 2 x 1024 | bytes written (exact, probes) | WRREQ | "
+                 "WRREQ_64B x 64")
+    vals = {}
+    for run in runs:
+        for ps in passes:
+            for r in _csv_rows(os.path.join(root, f"{ps}_{run}", "run_counter_collection.csv")):
+                m = re.search(r"gdn_stream_probe<(\d)>", r["Kernel_Name"])
+                name = (f"gdn_stream_probe<{m.group(1)}>" if m else
+                        "gdn_decode_rows<128,128,1,32>" if "gdn_decode_rows" in r["Kernel_Name"]
+                        else None)
+                if name:
+                    vals.setdefault((name, int(r["Grid_Size"])), {}).setdefault(
+                        r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    tile = 128 * 128 * 4
+    for (name, grid), c in sorted(vals.items()):
+        mean = {k: float(np.mean(v)) for k, v in c.items()}
+        tiles = grid // 256 * 2
+        kind = int(name[17]) if name.startswith("gdn_stream_probe") else None
+        rd = {0: tiles, 1: 0, 2: tiles, 3: tiles, 4: tiles}.get(kind)
+        wr = {0: None, 1: tiles, 2: tiles, 3: tiles, 4: 5 * tiles}.get(kind)
+        lines.append(" | ".join([
+            name, str(grid), "-" if rd is None else str(rd * tile),
+            f"{mean.get('TCC_EA0_RDREQ_sum', 0):.0f}", f"{mean.get('TCC_EA0_RDREQ_sum', 0) * 128:.0f}",
+            f"{mean.get('TCC_BUBBLE_sum', 0):.0f}", f"{mean.get('TCC_EA0_RDREQ_32B_sum', 0):.0f}",
+            f"{mean.get('FETCH_SIZE', 0) * 2048:.0f}", "-" if not wr else str(wr * tile),
+            f"{mean.get('TCC_EA0_WRREQ_sum', 0):.0f}", f"{mean.get('TCC_EA0_WRREQ_64B_sum', 0) * 64:.0f}"]))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "hbm_counters__crosscheck.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -380,6 +538,10 @@ def main():
     ap.add_argument("--family", type=int, default=0,
                     help="0 auto, 1 column tiles, 2 row split, 3 value rows (VK layout), "
                          "4 chunked (64-token chunks on the matrix cores)")
+    ap.add_argument("--chunk-form", default="workspace", choices=["workspace", "one-kernel"],
+                    help="where the chunked family runs: the prep + state-pass kernels over a "
+                         "workspace (gdn_chunk_gated_delta_rule_fwd with a workspace), or the "
+                         "one-kernel form")
     ap.add_argument("--layout", default="KV", choices=["KV", "VK"],
                     help="storage order of the state tiles")
     ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"],
@@ -403,6 +565,12 @@ def main():
     ap.add_argument("--summarize-stream", metavar="DIR",
                     help="instead: write profiles/stream_ceiling__decode_state_tiles.txt from a "
                          "rocprofv3 --kernel-trace of --stream-ceiling (CSV files in DIR)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead: time AUTO against every kernel family and tile over a grid of "
+                         "shapes and write profiles/auto_table__sweep.txt")
+    ap.add_argument("--summarize-counter-check", metavar="DIR",
+                    help="instead: write profiles/hbm_counters__crosscheck.txt from the raw TCC "
+                         "request counter passes under DIR")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="instead: write profiles/ summaries from rocprofv3 CSV output in DIR "
                          "(subdirectories trace, FETCH_SIZE, WRITE_SIZE, copy_FETCH_SIZE, "
@@ -419,6 +587,10 @@ def main():
     if args.summarize_utilization:
         summarize_utilization(args.summarize_utilization, args.workload, args.kernel, run,
                               args.state_dtype)
+        return
+
+    if args.summarize_counter_check:
+        summarize_counter_check(args.summarize_counter_check)
         return
 
     if args.summarize_stream:
@@ -456,6 +628,10 @@ def main():
 
     if args.stream_ceiling:
         stream_ceiling(args)
+        return
+
+    if args.sweep:
+        auto_sweep(args)
         return
 
     if args.copy_calibration:
@@ -511,6 +687,19 @@ def main():
     stream = torch.cuda.current_stream(dev)
     g_buf = torch.empty(inp.num_tokens, wl.num_v_heads, dtype=torch.float32, device=dev)
     beta_buf = torch.empty_like(g_buf)
+    info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
+                                        tokens_per_seq=wl.tokens_per_seq,
+                                        kernel_family=args.family, block_v=args.block_v,
+                                        block_k=args.block_k, waves_per_group=args.waves,
+                                        state_layout=args.layout),
+                        d["cu_seqlens"] is not None, inter is not None)
+    # The chunked family runs through its own entry point, by default over a
+    # workspace allocated here, outside the timed region.
+    chunk_ws = None
+    chunked = info.kernel_family == gdn.GDN_KERNEL_CHUNKED and not args.unfused
+    if chunked and args.chunk_form == "workspace":
+        chunk_ws = gdn.chunk_workspace(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
+                                       tokens_per_seq=wl.tokens_per_seq)
 
     def launch(i):
         # on torch's current stream: the timing stream, or the capture stream
@@ -522,6 +711,12 @@ def main():
                 d["cu_seqlens"], out, inter, tokens_per_seq=wl.tokens_per_seq,
                 kernel_family=args.family, block_v=args.block_v, block_k=args.block_k,
                 waves_per_group=args.waves, state_layout=args.layout)
+            return
+        if chunked:
+            gdn.gdn_chunk_gated_delta_rule_fwd(
+                d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool,
+                idx_sets[i % sets], d["cu_seqlens"], out, workspace=chunk_ws,
+                tokens_per_seq=wl.tokens_per_seq, state_layout=args.layout)
             return
         gdn.gdn_gating_delta_rule_update(
             d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"], pool,
@@ -569,19 +764,14 @@ def main():
     alg_bytes = W.algorithmic_bytes(inp, state_bytes=2 if args.state_dtype == "bf16" else 4)
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     value = updates * args.steps / wall
-    info = gdn.gdn_plan(gdn.make_config(d["q"], d["v"], pool, idx_sets[0], d["cu_seqlens"],
-                                        tokens_per_seq=wl.tokens_per_seq,
-                                        kernel_family=args.family, block_v=args.block_v,
-                                        block_k=args.block_k, waves_per_group=args.waves,
-                                        state_layout=args.layout),
-                        d["cu_seqlens"] is not None, inter is not None)
+    kname = kernel_name(info, chunk_ws is not None)
 
     # The committed counter profiles were taken with the library's tiling, the
     # KV layout and fused gates (fp32 state, or bf16 state under their own
     # file names); other runs get none.
     profiled = (args.layout == "KV" and not args.unfused
                 and not (args.block_v or args.block_k or args.waves))
-    traffic = (counter_traffic(kernel_name(info), wl.name, profile_variant(args.state_dtype))
+    traffic = (counter_traffic(kname, wl.name, profile_variant(args.state_dtype))
                if profiled else None)
     res = {
         "metric": METRIC,
@@ -601,7 +791,7 @@ def main():
                    "head_k_dim": wl.head_k_dim, "head_v_dim": wl.head_v_dim,
                    "activations": wl.act, "state": args.state_dtype, "state_layout": args.layout,
                    "pool_slots": wl.num_slots,
-                   "slot_sets": sets, "kernel": kernel_name(info),
+                   "slot_sets": sets, "kernel": kname,
                    "block_v": info.block_v, "block_k": info.block_k,
                    "waves_per_group": info.waves_per_group, "workgroups": info.workgroups,
                    "gates": "unfused pair (gdn_gating + gdn_recurrent_update)" if args.unfused
@@ -616,7 +806,7 @@ def main():
                      "traffic_gb_s": None if traffic is None else traffic / (kern_ms * 1e-3) / 1e9,
                      "traffic_frac": None if traffic is None
                                      else traffic / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "algorithmic_bytes": alg_bytes, "kernel": kernel_name(info)},
+                     "algorithmic_bytes": alg_bytes, "kernel": kname},
         "cpu_baseline": None,
     }
     if info.kernel_family == gdn.GDN_KERNEL_CHUNKED:
@@ -627,7 +817,7 @@ def main():
                            "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                            "traffic": traffic,
                            "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
-                           "kernel": KERNEL_NAMES[4]}
+                           "kernel": kname}
     else:
         # Token-by-token kernels: whichever of HBM and the fp32 VALU takes
         # longer at its peak bounds the call (long sequences: the VALU).
@@ -637,7 +827,7 @@ def main():
             res["roofline"] = {"bound": "alu", "achieved": tflops, "peak": VALU_FP32_PEAK_TFLOPS,
                                "unit": "TFLOP/s", "frac": tflops / VALU_FP32_PEAK_TFLOPS,
                                "traffic": traffic, "algorithmic_flops": flops,
-                               "algorithmic_bytes": alg_bytes, "kernel": kernel_name(info)}
+                               "algorithmic_bytes": alg_bytes, "kernel": kname}
     if args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(inp, pool_rows0, args.cpu_budget)
     print(json.dumps(res), flush=True)

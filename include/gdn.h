@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -243,26 +243,51 @@ gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, con
  * The chunked forward (prefill) of the same operation: the results of
  * gdn_gating_delta_rule_update with intermediate_states = NULL (outputs and
  * final states, up to fp32 rounding), computed 64 tokens at a time in the WY
- * form of the chunked gated delta rule.  sglang PR #21411 (implementation
- * section) fuses the chunk's K K^T, triangular solve and w/u recomputation
- * (chunk_gated_delta_rule_fwd, CHUNK_SIZE 64); here one workgroup per
- * (sequence, v-head) walks its chunks with the state resident on chip, so no
- * chunk index table is needed.  Meant for long sequences: the work per chunk
- * is dense matrix products, against one dependent step per token in the
- * per-token kernels.
+ * form of the chunked gated delta rule.  Meant for long sequences: the work
+ * per chunk is dense matrix products, against one dependent step per token
+ * in the per-token kernels.
  *
- * Arguments, layouts, alignment and the caller contract are those of
- * gdn_gating_delta_rule_update.  cfg->kernel_family must be GDN_KERNEL_AUTO
- * or GDN_KERNEL_CHUNKED, and block_v, block_k and waves_per_group must be 0.
- * K and V must be 32, 64 or 128, and 64 token rows of q, k, v or out must
- * span less than 2 GiB.  gdn_recurrent_update with kernel_family =
- * GDN_KERNEL_CHUNKED runs the same kernel on precomputed gates.
+ * With a workspace (the fast form), two kernels run.  sglang PR #21411
+ * (implementation section) builds a chunk's state-independent matrices --
+ * the key Gram product and the triangular solve -- in a kernel of its own
+ * over all chunks at once (chunk_gated_delta_rule_fwd, CHUNK_SIZE 64); here
+ * too a first kernel builds, for every (chunk, v-head) in parallel, the full
+ * inverse (I + L)^-1, the masked query-key products and the per-token
+ * decays into `workspace`; a second kernel then walks each (sequence,
+ * v-head)'s chunks in order with the state on chip, doing only the
+ * state-dependent products.  workspace must be 256-byte aligned and hold at
+ * least gdn_chunk_workspace_bytes(cfg) bytes (workspace_bytes says how many
+ * it holds); it is caller-owned device scratch whose contents on entry do not
+ * matter and on return are undefined.  Calls that run concurrently need
+ * separate workspaces.
+ *
+ * With workspace = NULL (workspace_bytes ignored), one kernel does
+ * everything: a workgroup per (sequence, v-head) builds each chunk's
+ * matrices itself before its state products.  No scratch memory is used; it
+ * is the form AUTO takes for long calls of gdn_gating_delta_rule_update.
+ *
+ * Arguments, layouts, alignment and the caller contract are otherwise those
+ * of gdn_gating_delta_rule_update.  cfg->kernel_family must be
+ * GDN_KERNEL_AUTO or GDN_KERNEL_CHUNKED, and block_v, block_k and
+ * waves_per_group must be 0.  K and V must be 32, 64 or 128, and 64 token
+ * rows of q, k, v, a, b or out must span less than 2 GiB.  A workspace that
+ * is misaligned or too small is rejected (GDN_ERR_MISALIGNED,
+ * GDN_ERR_BAD_ARGUMENT) before anything is launched.  gdn_recurrent_update
+ * with kernel_family = GDN_KERNEL_CHUNKED runs the one-kernel form on
+ * precomputed gates.
  */
 gdn_status gdn_chunk_gated_delta_rule_fwd(
     const void* q, const void* k, const void* v, const void* a, const void* b,
     const float* A_log, const float* dt_bias, void* state_pool,
     const int32_t* state_idx, const int32_t* cu_seqlens, void* out,
-    const gdn_config* cfg, void* stream);
+    void* workspace, size_t workspace_bytes, const gdn_config* cfg, void* stream);
+
+/* Bytes of workspace gdn_chunk_gated_delta_rule_fwd needs for `cfg`: one
+ * 21,760-byte entry per (chunk slot, v-head), with floor(num_tokens / 64) +
+ * num_seqs chunk slots (a sequence's chunks start at the slot after the
+ * previous sequence's, rounded to 64-token boundaries).  0 when cfg is NULL
+ * or describes no work (num_seqs or num_tokens 0), and for negative sizes. */
+size_t gdn_chunk_workspace_bytes(const gdn_config* cfg);
 
 /* Host-side argument check of gdn_gating_delta_rule_update (same arguments,
  * no stream); launches nothing and never touches device memory. */

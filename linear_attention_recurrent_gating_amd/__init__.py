@@ -40,7 +40,8 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
 
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_default_config", "gdn_gating_delta_rule_update", "gdn_gating",
-            "gdn_recurrent_update", "gdn_chunk_gated_delta_rule_fwd", "gdn_validate", "gdn_plan", "gdn_status_string",
+            "gdn_recurrent_update", "gdn_chunk_gated_delta_rule_fwd", "gdn_chunk_workspace_bytes",
+            "gdn_validate", "gdn_plan", "gdn_status_string",
             "gdn_last_error_message", "gdn_abi_version")
 
 
@@ -88,8 +89,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn_gating.restype = ctypes.c_int
     lib.gdn_recurrent_update.argtypes = [P] * 10 + [C, P]
     lib.gdn_recurrent_update.restype = ctypes.c_int
-    lib.gdn_chunk_gated_delta_rule_fwd.argtypes = [P] * 11 + [C, P]
+    lib.gdn_chunk_gated_delta_rule_fwd.argtypes = [P] * 12 + [ctypes.c_size_t, C, P]
     lib.gdn_chunk_gated_delta_rule_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_workspace_bytes.argtypes = [C]
+    lib.gdn_chunk_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_validate.argtypes = [P] * 12 + [C]
     lib.gdn_validate.restype = ctypes.c_int
     lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
@@ -338,12 +341,15 @@ class PreparedUpdate:
 
 
 def gdn_chunk_gated_delta_rule_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx,
-                                   cu_seqlens=None, out=None, *, tokens_per_seq=None,
-                                   scale: float = 0.0, eps: float = 1e-6, flags: int = 0,
-                                   stream=None, state_layout=GDN_LAYOUT_KV):
+                                   cu_seqlens=None, out=None, *, workspace=None,
+                                   tokens_per_seq=None, scale: float = 0.0, eps: float = 1e-6,
+                                   flags: int = 0, stream=None, state_layout=GDN_LAYOUT_KV):
     """The chunked forward (64-token chunks on the matrix cores): the outputs
     and final states of gdn_gating_delta_rule_update without intermediate
-    states.  Arguments as there; K and V must be 32, 64 or 128.  Returns ``out``."""
+    states.  Arguments as there; K and V must be 32, 64 or 128.  workspace:
+    None runs the one-kernel form; a CUDA tensor (any dtype, contiguous, at
+    least gdn_chunk_workspace_bytes(...) bytes, see chunk_workspace) runs the
+    two-kernel form over it.  Returns ``out``."""
     import torch
     if out is None:
         out = torch.empty(v.shape, dtype=v.dtype, device=v.device)
@@ -351,11 +357,30 @@ def gdn_chunk_gated_delta_rule_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, st
                    state_layout)
     cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
                       scale=scale, eps=eps, flags=flags, k=k, state_layout=state_layout, a=a, b=b)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     stream = _stream_handle(stream, q.device)
     _check(raw_library().gdn_chunk_gated_delta_rule_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
-        _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out), ctypes.byref(cfg), stream))
+        _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out), ws_ptr, ws_bytes,
+        ctypes.byref(cfg), stream))
     return out
+
+
+def gdn_chunk_workspace_bytes(cfg: GdnConfig) -> int:
+    """Workspace bytes the two-kernel chunked form needs for cfg."""
+    return int(raw_library().gdn_chunk_workspace_bytes(ctypes.byref(cfg)))
+
+
+def chunk_workspace(q, v, state_pool, state_idx, cu_seqlens=None, *, tokens_per_seq=None):
+    """A device byte tensor big enough to be the workspace of
+    gdn_chunk_gated_delta_rule_fwd on these tensors (PyTorch allocates it)."""
+    import torch
+    cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq)
+    return torch.empty(max(1, gdn_chunk_workspace_bytes(cfg)), dtype=torch.uint8, device=q.device)
 
 
 def gdn_gating(a, b, A_log, dt_bias, g=None, beta=None, *, num_k_heads=None, stream=None):

@@ -528,14 +528,31 @@ gdn_status validate_update(const void* q, const void* k, const void* v, const vo
     return GDN_OK;
 }
 
+// Bytes of the two-kernel chunked form's workspace (0 for no work).
+size_t chunk_workspace_bytes(const gdn_config& c) {
+    if (c.num_seqs <= 0 || c.num_tokens <= 0 || c.num_v_heads < 1) return 0;
+    return static_cast<size_t>(gdn::chunk_ws_slots(c.num_tokens, c.num_seqs)) *
+           static_cast<size_t>(c.num_v_heads) * static_cast<size_t>(gdn::chunk_ws_entry_bytes());
+}
+
+// workspace (chunked family only): NULL runs the one-kernel form; otherwise
+// at least chunk_workspace_bytes(cfg), 256-byte aligned.
 gdn_status run_update(const void* q, const void* k, const void* v, const void* a, const void* b,
                       const float* A_log, const float* dt_bias, const float* g, const float* beta,
                       void* state_pool, const int32_t* state_idx, const int32_t* cu_seqlens,
-                      void* out, void* intermediate_states, const gdn_config* cfg, void* stream) {
+                      void* out, void* intermediate_states, const gdn_config* cfg, void* stream,
+                      void* workspace = nullptr, size_t workspace_bytes = 0) {
     gdn_status s = validate_update(q, k, v, a, b, A_log, dt_bias, g, beta, state_pool, state_idx,
                                    cu_seqlens, out, intermediate_states, cfg);
     if (s != GDN_OK) return s;
     const gdn_config& c = *cfg;
+    if (workspace) {
+        if (!aligned(workspace, 256))
+            return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+        if (workspace_bytes < chunk_workspace_bytes(c))
+            return fail(GDN_ERR_BAD_ARGUMENT, "workspace holds %zu bytes; this call needs %zu",
+                        workspace_bytes, chunk_workspace_bytes(c));
+    }
     if (c.num_seqs == 0 || c.num_tokens == 0) return GDN_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (c.flags & GDN_FLAG_DEBUG_CHECKS) {
@@ -592,15 +609,18 @@ gdn_status run_update(const void* q, const void* k, const void* v, const void* a
                      "waves=%d chunk=%d groups=%lld lds=%d\n",
                      sh.kind == gdn::kKindRows        ? "rows"
                      : sh.kind == gdn::kKindValueRows ? "value-rows"
-                     : sh.kind == gdn::kKindChunked   ? "chunked"
+                     : sh.kind == gdn::kKindChunked   ? (workspace ? "chunked (prep + state pass)"
+                                                                   : "chunked")
                                                       : "columns",
                      sh.K, c.head_v_dim, sh.act ? "bf16" : "f32", p.state_bf16 ? "bf16" : "f32",
                      g ? "precomputed" : "fused",
                      sh.multi_token, sh.block_v, sh.block_k, sh.waves, sh.chunk,
                      static_cast<long long>(sh.groups), sh.lds_bytes);
 
-    const hipError_t e = sh.kind == gdn::kKindChunked ? gdn::launch_chunked(sh, p, st)
-                                                      : gdn::launch_fused(sh, p, st);
+    const hipError_t e =
+        sh.kind != gdn::kKindChunked ? gdn::launch_fused(sh, p, st)
+        : workspace ? gdn::launch_chunked_ws(sh, p, c.num_seqs, c.num_tokens, workspace, st)
+                    : gdn::launch_chunked(sh, p, st);
     if (e != hipSuccess)
         return fail(GDN_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
     return GDN_OK;
@@ -665,7 +685,8 @@ gdn_status gdn_chunk_gated_delta_rule_fwd(const void* q, const void* k, const vo
                                           const void* a, const void* b, const float* A_log,
                                           const float* dt_bias, void* state_pool,
                                           const int32_t* state_idx, const int32_t* cu_seqlens,
-                                          void* out, const gdn_config* cfg, void* stream) {
+                                          void* out, void* workspace, size_t workspace_bytes,
+                                          const gdn_config* cfg, void* stream) {
     g_last_error[0] = '\0';
     if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
     if (cfg->kernel_family != GDN_KERNEL_AUTO && cfg->kernel_family != GDN_KERNEL_CHUNKED)
@@ -674,7 +695,11 @@ gdn_status gdn_chunk_gated_delta_rule_fwd(const void* q, const void* k, const vo
     gdn_config c = *cfg;
     c.kernel_family = GDN_KERNEL_CHUNKED;
     return run_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
-                      cu_seqlens, out, nullptr, &c, stream);
+                      cu_seqlens, out, nullptr, &c, stream, workspace, workspace_bytes);
+}
+
+size_t gdn_chunk_workspace_bytes(const gdn_config* cfg) {
+    return cfg ? chunk_workspace_bytes(*cfg) : 0;
 }
 
 gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,

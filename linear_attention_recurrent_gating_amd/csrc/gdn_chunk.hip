@@ -204,19 +204,19 @@ gdn_chunk_fwd(const FusedParams p) {
                 const uint32_t grow = static_cast<uint32_t>(p.Hv) * 4;
                 const auto gr = buffer_rsrc(p.g + u0 * p.Hv + h, (Ln - 1) * grow + 4);
                 const auto br = buffer_rsrc(p.beta + u0 * p.Hv + h, (Ln - 1) * grow + 4);
-                L.ga = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, lane * grow, 0, 0));
-                L.gb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, lane * grow, 0, 0));
+                L.ga = __builtin_amdgcn_raw_buffer_load_b32(gr, lane * grow, 0, 0);
+                L.gb = __builtin_amdgcn_raw_buffer_load_b32(br, lane * grow, 0, 0);
             } else {
                 const int64_t e0 = u0 * p.ab_stride + static_cast<int64_t>(h / p.G) * p.ab_khead + h % p.G;
                 const uint32_t abrow = static_cast<uint32_t>(p.ab_stride) * esz;
                 const auto ar = buffer_rsrc(static_cast<const char*>(p.a) + e0 * esz, (Ln - 1) * abrow + esz);
                 const auto br = buffer_rsrc(static_cast<const char*>(p.b) + e0 * esz, (Ln - 1) * abrow + esz);
                 if constexpr (ACT == 0) {
-                    L.ga = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ar, lane * abrow, 0, 0));
-                    L.gb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, lane * abrow, 0, 0));
+                    L.ga = __builtin_amdgcn_raw_buffer_load_b32(ar, lane * abrow, 0, 0);
+                    L.gb = __builtin_amdgcn_raw_buffer_load_b32(br, lane * abrow, 0, 0);
                 } else {
-                    L.ga = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(ar, lane * abrow, 0, 0)) << 16);
-                    L.gb = __uint_as_float(uint32_t(__builtin_amdgcn_raw_buffer_load_b16(br, lane * abrow, 0, 0)) << 16);
+                    L.ga = __builtin_amdgcn_raw_buffer_load_b16(ar, lane * abrow, 0, 0);
+                    L.gb = __builtin_amdgcn_raw_buffer_load_b16(br, lane * abrow, 0, 0);
                 }
             }
         }
@@ -285,10 +285,11 @@ gdn_chunk_fwd(const FusedParams p) {
         if (wave == 0) {
             float glog, bet;
             if (p.g) {
-                glog = L.ga;
-                bet = L.gb;
+                glog = __uint_as_float(L.ga);
+                bet = __uint_as_float(L.gb);
             } else {
-                gate_values(L.ga, L.gb, A_h, dtb_h, glog, bet);
+                const uint32_t sh = ACT == 0 ? 0 : 16;   // bf16 in the low half
+                gate_values(__uint_as_float(L.ga << sh), __uint_as_float(L.gb << sh), A_h, dtb_h, glog, bet);
             }
             if (lane >= Ln) glog = bet = 0.0f;  // padding tokens: no decay, no update
             const double G = wave_prefix_sum(static_cast<double>(glog));
@@ -309,8 +310,14 @@ gdn_chunk_fwd(const FusedParams p) {
         issue_loads(0, ld0);
         stage(0, ld0);
     }
+    // Past the last chunk the loads and staging below repeat the last
+    // chunk's loads (in bounds) and stage into the other scalar buffer and
+    // the key/query rows, which nothing reads any more: every iteration then
+    // issues the same loads in the same order, and each wait covers exactly
+    // the loads it needs.
+    const int last = nchunks - 1;
     ChunkLoads<ACT, NQK> ld;
-    if (nchunks > 1) issue_loads(1, ld);
+    issue_loads(min(1, last), ld);
 
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = bos + static_cast<int64_t>(c) * kC;
@@ -557,10 +564,8 @@ gdn_chunk_fwd(const FusedParams p) {
 
         // The next chunk: stage it (its rows of kt/qt are no longer read) and
         // issue the loads of the one after.
-        if (c + 1 < nchunks) {
-            stage(c + 1, ld);
-            if (c + 2 < nchunks) issue_loads(c + 2, ld);
-        }
+        stage(c + 1, ld);
+        issue_loads(min(c + 2, last), ld);
 
         // --------------------------------------- E: u, outputs, state update
         // U = (I + L)^-1 R by block forward substitution on this wave's

@@ -166,12 +166,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Staging loads of one chunk, issued a chunk ahead so that they land while
 // the previous chunk's products run: raw keys and queries (16-byte vectors,
 // NQK per lane) and the raw gate inputs of token `lane` (wave 0).
+// The gate inputs stay raw words until staging (a bf16 value in the low
+// half): widening them next to their loads would make the wave wait there
+// for every load issued before, the key/query prefetch included.
 template <int ACT, int NQK>
 struct ChunkLoads {
     static constexpr int VEC = ACT == 0 ? 2 : 1;   // 16-byte vectors per 8 elements
     u32x4v k[NQK][VEC];
     u32x4v q[NQK][VEC];
-    float ga, gb;
+    uint32_t ga, gb;
 };
 
 }  // namespace

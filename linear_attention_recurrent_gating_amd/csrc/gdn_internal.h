@@ -106,6 +106,15 @@ constexpr int kChunkedTokens = 64;
 // Enqueues the chunked kernel (grid = sequences x v-heads).
 hipError_t launch_chunked(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);
 
+// The two-kernel chunked form over a workspace: bytes of one (chunk slot,
+// v-head) entry, the chunk slots of a call (entries = slots x H_v), and the
+// launch of the prep kernel (slots x H_v workgroups) and the state pass
+// (the chunked kernel's grid).
+int64_t chunk_ws_entry_bytes();
+int64_t chunk_ws_slots(int64_t num_tokens, int num_seqs);
+hipError_t launch_chunked_ws(const LaunchShape& shape, const FusedParams& p, int num_seqs,
+                             int64_t num_tokens, void* workspace, hipStream_t stream);
+
 // Enqueues the fused kernel; returns the HIP launch status.
 hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);
 

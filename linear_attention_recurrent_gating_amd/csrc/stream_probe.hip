@@ -23,7 +23,33 @@ constexpr int kTileBytes = 64 * 1024;
 constexpr int kRows = 32;            // 128-bit accesses per lane per tile half
 constexpr uint32_t kRowStep = 1024;  // bytes between a lane's accesses
 
-enum Kind { kRead = 0, kWrite = 1, kRmw = 2, kCopy = 3, kSpec = 4 };
+enum Kind { kRead = 0, kWrite = 1, kRmw = 2, kCopy = 3, kSpec = 4, kRmwBf16 = 5 };
+
+// bf16 state tiles (32 KiB): the row-split kernel's bf16 access, 8 bytes
+// (four elements) per lane, so one 64-bit instruction moves two 256-byte rows;
+// 32 of them per lane, two wavefronts per tile, in place.
+__global__ void __launch_bounds__(256) gdn_stream_probe_bf16(char* pool, const int32_t* tiles,
+                                                             float scale) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    constexpr int kBytes = kTileBytes / 2;
+    const int wave = threadIdx.x / 64;
+    const int lane = threadIdx.x % 64;
+    const int64_t slot = static_cast<int64_t>(blockIdx.x) * 2 + wave / 2;
+    const int64_t tile = tiles[slot];
+    const uint32_t lane_bytes = (wave % 2) * (kBytes / 2) + (lane / 32) * 256 + (lane % 32) * 8;
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(pool + tile * kBytes, 0, kBytes, kWord3);
+    u32x2 x[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i)
+        x[i] = __builtin_amdgcn_raw_buffer_load_b64(r, lane_bytes, i * 512, kBufNonTemporal);
+    const uint32_t s = scale == 1.0f ? 0u : 0x00010001u;   // adds nothing unless scale != 1
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+        x[i].x += s;
+        x[i].y += s;
+        __builtin_amdgcn_raw_buffer_store_b64(x[i], r, lane_bytes, i * 512, kBufNonTemporal);
+    }
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, kTileBytes, kWord3);
@@ -101,8 +127,9 @@ extern "C" {
 // indices), 4 the spec-verify pattern (read once, write four intermediate
 // tiles of `dst` laid out as described above for `heads` heads per
 // sequence, then write in place; num_tiles a multiple of heads, dst holding
-// 4 * num_tiles tiles).  `sink` holds num_tiles * 128 floats (read only).
-// Returns a hipError_t.
+// 4 * num_tiles tiles), 5 in-place read-modify-write of 32 KiB bf16 tiles
+// (tile i at byte offset 32 KiB x i of `pool`).  `sink` holds num_tiles *
+// 128 floats (read only).  Returns a hipError_t.
 int gdn_stream_probe_launch(int kind, const void* pool, void* dst, const int32_t* tiles,
                             int64_t num_tiles, float* sink, float scale, int heads, void* stream) {
     if (num_tiles <= 0 || num_tiles % 2 != 0 || heads <= 0 || num_tiles % heads != 0)
@@ -117,6 +144,7 @@ int gdn_stream_probe_launch(int kind, const void* pool, void* dst, const int32_t
         case kRmw: hipLaunchKernelGGL(gdn_stream_probe<kRmw>, grid, block, 0, s, p, d, tiles, sink, scale, heads); break;
         case kCopy: hipLaunchKernelGGL(gdn_stream_probe<kCopy>, grid, block, 0, s, p, d, tiles, sink, scale, heads); break;
         case kSpec: hipLaunchKernelGGL(gdn_stream_probe<kSpec>, grid, block, 0, s, p, d, tiles, sink, scale, heads); break;
+        case kRmwBf16: hipLaunchKernelGGL(gdn_stream_probe_bf16, grid, block, 0, s, const_cast<char*>(p), tiles, scale); break;
         default: return static_cast<int>(hipErrorInvalidValue);
     }
     return static_cast<int>(hipGetLastError());

@@ -46,7 +46,7 @@ def test_header_and_c_example_compile_as_c11():
 
 
 def test_abi_version_and_status_strings():
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == 2
     seen = set()
     for code in range(0, 8):
         s = gdn.gdn_status_string(code)
@@ -415,20 +415,40 @@ def test_chunked_ab_stride_offsets():
 
 def test_chunked_entry_point_validation():
     lib = gdn.raw_library()
-    c = base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT)
-    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ctypes.byref(c),
-                                              None) == 7
-    c = base_cfg(head_k_dim=256)
-    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ctypes.byref(c),
-                                              None) == 3
-    c = base_cfg()
-    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, None, ctypes.byref(c),
-                                              None) == 1
-    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], None, None) == 1
+
+    def call(c, out=A[10], ws=None, ws_bytes=0):
+        return lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, out, ws, ws_bytes,
+                                                  None if c is None else ctypes.byref(c), None)
+    assert call(base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT)) == 7
+    assert call(base_cfg(head_k_dim=256)) == 3
+    assert call(base_cfg(), out=None) == 1
+    assert call(None) == 1
     # a zero-sequence batch returns before touching anything
-    c = base_cfg(num_seqs=0, num_tokens=0)
-    assert lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ctypes.byref(c),
-                                              None) == 0
+    assert call(base_cfg(num_seqs=0, num_tokens=0)) == 0
+
+
+def test_chunk_workspace_size_and_checks():
+    """The workspace of the two-kernel form: one 21,760-byte entry per (chunk
+    slot, v-head), floor(N / 64) + B slots; a workspace that is too small or
+    not 256-byte aligned is rejected before any launch."""
+    lib = gdn.raw_library()
+    entry = 21760
+    c = base_cfg(num_seqs=3, tokens_per_seq=100, num_tokens=300)   # 4 v-heads
+    need = gdn.gdn_chunk_workspace_bytes(c)
+    assert need == (300 // 64 + 3) * 4 * entry
+    assert gdn.gdn_chunk_workspace_bytes(base_cfg(num_seqs=0, num_tokens=0)) == 0
+    assert lib.gdn_chunk_workspace_bytes(None) == 0
+    ws = 0x7f1000000000            # fake, never dereferenced; 256-byte aligned
+
+    def call(ws_ptr, nbytes):
+        return lib.gdn_chunk_gated_delta_rule_fwd(*A[:7], A[7], A[8], None, A[10], ws_ptr, nbytes,
+                                                  ctypes.byref(c), None)
+    assert call(ws, need - 1) == 7
+    assert "needs" in gdn.gdn_last_error_message()
+    assert call(ws + 128, need) == 5
+    # a varlen call: every sequence may start a new slot
+    v = base_cfg(num_seqs=5, num_tokens=129, num_slots=8)
+    assert gdn.gdn_chunk_workspace_bytes(v) == (129 // 64 + 5) * 4 * entry
 
 
 def test_ab_stride_validation():

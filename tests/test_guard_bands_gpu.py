@@ -46,7 +46,7 @@ class Guarded:
         self.n = int(np.prod(shape)) if len(shape) else 1
         self.whole = torch.empty(self.n + 2 * self.m, dtype=dtype, device=dev)
         if fill_bits is not None:
-            ityp = {4: torch.int32, 2: torch.int16}[esize]
+            ityp = {4: torch.int32, 2: torch.int16, 1: torch.uint8}[esize]
             bits = fill_bits if fill_bits < 2 ** (8 * esize - 1) else fill_bits - 2 ** (8 * esize)
             self.whole.view(ityp).fill_(bits)
         else:
@@ -57,7 +57,7 @@ class Guarded:
     def margins(self):
         import torch
         w = self.whole
-        ityp = {4: torch.int32, 2: torch.int16, 8: torch.int64}[w.element_size()]
+        ityp = {4: torch.int32, 2: torch.int16, 8: torch.int64, 1: torch.uint8}[w.element_size()]
         raw = w.view(ityp)
         return raw[:self.m].cpu().clone(), raw[self.m + self.n:].cpu().clone()
 
@@ -89,7 +89,7 @@ def edge_slots(inp, num_slots, seed):
 
 
 def run_guarded(inp, pool_np, dev, layout="KV", family=0, state_bf16=False, pregated=False,
-                chunked_entry=False, flags=0):
+                chunked_entry=False, flags=0, workspace=False):
     """One call with every tensor in a guard band.  Returns (out, inter,
     pool after) as numpy arrays and checks every margin."""
     import torch
@@ -135,8 +135,17 @@ def run_guarded(inp, pool_np, dev, layout="KV", family=0, state_bf16=False, preg
                                  tokens_per_seq=wl.tokens_per_seq, kernel_family=family,
                                  state_layout=layout, flags=flags)
     elif chunked_entry:
+        ws = None
+        if workspace:   # the two-kernel form's scratch, in a guard band of its own
+            need = gdn.chunk_workspace(gq.t, gv.t, gpool.t, gidx.t, cu,
+                                       tokens_per_seq=wl.tokens_per_seq).numel()
+            gws = Guarded((need,), torch.uint8, dev, fill_bits=0xA5)
+            gws.t.fill_(0xFF)
+            gated = [(gws, "workspace")]
+            ws = gws.t
         gdn.gdn_chunk_gated_delta_rule_fwd(gq.t, gk.t, gv.t, ga.t, gb.t, gA.t, gdt.t, gpool.t,
-                                           gidx.t, cu, gout.t, tokens_per_seq=wl.tokens_per_seq,
+                                           gidx.t, cu, gout.t, workspace=ws,
+                                           tokens_per_seq=wl.tokens_per_seq,
                                            state_layout=layout, flags=flags)
     else:
         gdn.gdn_gating_delta_rule_update(gq.t, gk.t, gv.t, ga.t, gb.t, gA.t, gdt.t, gpool.t,
@@ -189,7 +198,8 @@ def ragged_last(wl, last_len):
 
 
 CASES = [
-    # (id, workload, ragged last length or None, layout, family, state bf16, pregated, chunked)
+    # (id, workload, ragged last length or None, layout, family, state bf16, pregated, chunked:
+    #  False, True (one kernel) or "workspace")
     ("rows_decode", W.Workload("gb_rows_decode", 300, 12, 1, 2, 4, 128, 128, W.ACT_BF16, 16,
                                0.05, num_padded=2), None, "KV", 2, False, False, False),
     ("rows_decode_f32_k64", W.Workload("gb_rows_k64", 301, 9, 1, 2, 4, 64, 128, W.ACT_F32, 11,
@@ -214,6 +224,12 @@ CASES = [
     ("chunked_f32_vk", W.Workload("gb_chunk_f32", 308, 4, 1, 2, 4, 64, 64, W.ACT_F32, 7, 0.1,
                                   varlen=True, len_range=(20, 150)), 77, "VK", 4, False, False,
      True),
+    ("chunked_workspace", W.Workload("gb_chunk_ws", 310, 5, 1, 2, 4, 128, 128, W.ACT_BF16, 8,
+                                     0.05, varlen=True, len_range=(30, 200), num_padded=1), 131,
+     "KV", 4, False, False, "workspace"),
+    ("chunked_workspace_f32_vk", W.Workload("gb_chunk_ws_f32", 311, 4, 1, 2, 4, 64, 64, W.ACT_F32,
+                                            7, 0.1, varlen=True, len_range=(20, 150)), 77, "VK", 4,
+     False, False, "workspace"),
     ("unfused_pair", W.Workload("gb_unfused", 309, 6, 1, 2, 4, 128, 128, W.ACT_BF16, 9, 0.05,
                                 varlen=True, len_range=(1, 6), num_padded=1,
                                 intermediates=True), 3, "KV", 0, False, True, False),
@@ -240,7 +256,8 @@ def test_guard_bands(dev, case):
         pool_np = pool_f32
     out, inter, pool_after = run_guarded(inp, pool_np, dev, layout=layout, family=family,
                                          state_bf16=state_bf16, pregated=pregated,
-                                         chunked_entry=chunked)
+                                         chunked_entry=bool(chunked),
+                                         workspace=chunked == "workspace")
     if state_bf16:
         # bf16 storage: outputs to the activation bar, stored states within
         # 2^-8 of the oracle's (one rounding), untouched slots bit-identical
