@@ -289,6 +289,30 @@ gdn_status gdn_chunk_gated_delta_rule_fwd(
  * or describes no work (num_seqs or num_tokens 0), and for negative sizes. */
 size_t gdn_chunk_workspace_bytes(const gdn_config* cfg);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * two-kernel form of gdn_chunk_gated_delta_rule_fwd over the library's own
+ * fixed device scratch instead of a caller workspace.  Same arguments without
+ * the workspace, same results bit for bit.
+ *
+ * The scratch is GDN_CHUNK_SCRATCH_BYTES (128 MiB) of device memory that each
+ * GPU the library runs on holds until the process ends.  A call that needs
+ * more (gdn_chunk_workspace_bytes(cfg) > GDN_CHUNK_SCRATCH_BYTES: (floor(N /
+ * 64) + B) x H_v above 6168 chunk entries, e.g. about 11.8k tokens over 8
+ * sequences at 32 v-heads) is rejected with GDN_ERR_BAD_ARGUMENT before
+ * anything is launched.  Nothing in it needs clearing between calls.  Every
+ * call on one GPU uses the same scratch: calls that may overlap on a GPU
+ * (other streams, or host threads without ordering between them) race, and
+ * the caller must serialise them.  The call allocates and frees nothing.
+ */
+#define GDN_CHUNK_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_chunk_gated_delta_rule_fwd_noalloc(
+    const void* q, const void* k, const void* v, const void* a, const void* b,
+    const float* A_log, const float* dt_bias, void* state_pool,
+    const int32_t* state_idx, const int32_t* cu_seqlens, void* out,
+    const gdn_config* cfg, void* stream);
+
 /* Host-side argument check of gdn_gating_delta_rule_update (same arguments,
  * no stream); launches nothing and never touches device memory. */
 gdn_status gdn_validate(

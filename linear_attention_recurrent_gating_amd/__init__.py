@@ -41,6 +41,7 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL_POINTER", 2: "GDN_ERR_BAD_SHAPE",
 # Every symbol include/gdn.h declares.
 EXPORTED = ("gdn_default_config", "gdn_gating_delta_rule_update", "gdn_gating",
             "gdn_recurrent_update", "gdn_chunk_gated_delta_rule_fwd", "gdn_chunk_workspace_bytes",
+            "gdn_chunk_gated_delta_rule_fwd_noalloc",
             "gdn_validate", "gdn_plan", "gdn_status_string",
             "gdn_last_error_message", "gdn_abi_version")
 
@@ -93,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_chunk_gated_delta_rule_fwd.restype = ctypes.c_int
     lib.gdn_chunk_workspace_bytes.argtypes = [C]
     lib.gdn_chunk_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_gated_delta_rule_fwd_noalloc.argtypes = [P] * 11 + [C, P]
+    lib.gdn_chunk_gated_delta_rule_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_validate.argtypes = [P] * 12 + [C]
     lib.gdn_validate.restype = ctypes.c_int
     lib.gdn_plan.argtypes = [C, ctypes.c_int, ctypes.c_int, ctypes.POINTER(GdnLaunchInfo)]
@@ -367,6 +370,25 @@ def gdn_chunk_gated_delta_rule_fwd(q, k, v, a, b, A_log, dt_bias, state_pool, st
         _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
         _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out), ws_ptr, ws_bytes,
         ctypes.byref(cfg), stream))
+    return out
+
+
+def gdn_chunk_gated_delta_rule_fwd_noalloc(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx,
+                                           cu_seqlens, out, *, tokens_per_seq=None,
+                                           scale: float = 0.0, eps: float = 1e-6, flags: int = 0,
+                                           stream=None, state_layout=GDN_LAYOUT_KV):
+    """The two-kernel chunked forward over the library's fixed device scratch
+    (no workspace argument, nothing allocated by the call; ``out`` must be
+    given).  Calls that may overlap on one GPU share that scratch and race.
+    Returns ``out``."""
+    _check_tensors(q, k, v, a, b, A_log, dt_bias, state_pool, state_idx, cu_seqlens, out, None,
+                   state_layout)
+    cfg = make_config(q, v, state_pool, state_idx, cu_seqlens, tokens_per_seq=tokens_per_seq,
+                      scale=scale, eps=eps, flags=flags, k=k, state_layout=state_layout, a=a, b=b)
+    stream = _stream_handle(stream, q.device)
+    _check(raw_library().gdn_chunk_gated_delta_rule_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), _ptr(out), ctypes.byref(cfg), stream))
     return out
 
 

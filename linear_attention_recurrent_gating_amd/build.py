@@ -22,7 +22,7 @@ C_EXAMPLE = os.path.join(LIBDIR, "c_abi_decode")
 PROBE_SRC = os.path.join(CSRC, "stream_probe.hip")
 PROBE_LIB = os.path.join(LIBDIR, "libgdn_stream_probe.so")
 
-DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_rows.hip", "gdn_chunk.hip", "gdn_chunk_ws.hip"]
+DEVICE_SOURCES = ["gdn_kernels.hip", "gdn_rows.hip", "gdn_chunk.hip", "gdn_chunk_ws.hip", "gdn_scratch.hip"]
 HOST_SOURCES = ["gdn_api.cpp"]
 
 # Packed fp32 VALU forms are disabled: hipcc -O3 otherwise forms them from

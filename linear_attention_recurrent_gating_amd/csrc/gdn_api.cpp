@@ -702,6 +702,42 @@ size_t gdn_chunk_workspace_bytes(const gdn_config* cfg) {
     return cfg ? chunk_workspace_bytes(*cfg) : 0;
 }
 
+gdn_status gdn_chunk_gated_delta_rule_fwd_noalloc(const void* q, const void* k, const void* v,
+                                                  const void* a, const void* b, const float* A_log,
+                                                  const float* dt_bias, void* state_pool,
+                                                  const int32_t* state_idx,
+                                                  const int32_t* cu_seqlens, void* out,
+                                                  const gdn_config* cfg, void* stream) {
+    g_last_error[0] = '\0';
+    if (!cfg) return fail(GDN_ERR_NULL_POINTER, "cfg is NULL");
+    if (cfg->kernel_family != GDN_KERNEL_AUTO && cfg->kernel_family != GDN_KERNEL_CHUNKED)
+        return fail(GDN_ERR_BAD_ARGUMENT, "kernel_family = %d: the chunked forward runs "
+                                          "GDN_KERNEL_CHUNKED only", cfg->kernel_family);
+    gdn_config c = *cfg;
+    c.kernel_family = GDN_KERNEL_CHUNKED;
+    gdn_status s = validate_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool,
+                                   state_idx, cu_seqlens, out, nullptr, &c);
+    if (s != GDN_OK) return s;
+    const size_t need = chunk_workspace_bytes(c);
+    if (need > gdn::scratch_bytes())
+        return fail(GDN_ERR_BAD_ARGUMENT, "this call needs %zu bytes of scratch; the library's "
+                                          "fixed scratch holds %zu (GDN_CHUNK_SCRATCH_BYTES): pass "
+                                          "a workspace to gdn_chunk_gated_delta_rule_fwd instead",
+                    need, gdn::scratch_bytes());
+    if (need == 0) return GDN_OK;   // no sequence or no token: nothing to do
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "cannot tell the stream's device: %s", hipGetErrorString(e));
+    void* ws = nullptr;
+    e = gdn::scratch_address(dev, &ws);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_LAUNCH, "looking up the device scratch failed: %s", hipGetErrorString(e));
+    return run_update(q, k, v, a, b, A_log, dt_bias, nullptr, nullptr, state_pool, state_idx,
+                      cu_seqlens, out, nullptr, &c, stream, ws, gdn::scratch_bytes());
+}
+
 gdn_status gdn_recurrent_update(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, void* state_pool, const int32_t* state_idx,
                                 const int32_t* cu_seqlens, void* out, void* intermediate_states,

@@ -115,6 +115,12 @@ int64_t chunk_ws_slots(int64_t num_tokens, int num_seqs);
 hipError_t launch_chunked_ws(const LaunchShape& shape, const FusedParams& p, int num_seqs,
                              int64_t num_tokens, void* workspace, hipStream_t stream);
 
+// The library's fixed device scratch (gdn_scratch.hip), the workspace of the
+// allocation-free chunked entry point: its size, and its address on `device`
+// (looked up with that device current on the first call for it).
+size_t scratch_bytes();
+hipError_t scratch_address(int device, void** out);
+
 // Enqueues the fused kernel; returns the HIP launch status.
 hipError_t launch_fused(const LaunchShape& shape, const FusedParams& p, hipStream_t stream);
 

@@ -485,3 +485,24 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "libgdn.so"))
     with pytest.raises(ImportError, match="not built"):
         gdn._load()
+
+
+def test_noalloc_entry_point_rejections():
+    """The allocation-free chunked entry point checks its arguments, and that
+    the call fits the library's 128 MiB scratch, before it looks at any
+    device: a call needing more is rejected with GDN_ERR_BAD_ARGUMENT."""
+    lib = gdn.raw_library()
+
+    def call(c, out=A[10]):
+        return lib.gdn_chunk_gated_delta_rule_fwd_noalloc(*A[:7], A[7], A[8], None, out,
+                                                          None if c is None else ctypes.byref(c),
+                                                          None)
+    assert call(None) == 1
+    assert call(base_cfg(kernel_family=gdn.GDN_KERNEL_ROW_SPLIT)) == 7
+    assert call(base_cfg(head_k_dim=256)) == 3
+    assert call(base_cfg(), out=None) == 1
+    assert call(base_cfg(num_seqs=0, num_tokens=0)) == 0
+    big = base_cfg(num_seqs=2, tokens_per_seq=64 * 800, num_tokens=2 * 64 * 800, num_slots=4)
+    assert gdn.gdn_chunk_workspace_bytes(big) > 128 << 20
+    assert call(big) == 7
+    assert "scratch" in gdn.gdn_last_error_message()
