@@ -153,6 +153,11 @@ def cpu_baseline(inp, pool_rows: np.ndarray, budget_s: float):
             "single_core_sample": f"the same batch on 1 thread, repeated {reps1}x over {el1:.1f} s"}
 
 
+def kernel_parts(kernel: str):
+    """The kernels of one step: a name of the form "a+b" is a step of two."""
+    return kernel.split("+")
+
+
 def _csv_rows(path):
     import csv
     with open(path, newline="") as f:
@@ -178,34 +183,42 @@ def summarize_profiles(prof_dir: str, workload: str, kernel: str, commands: dict
         lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}")
-    # per-dispatch durations of the measured kernel from the trace records
+    # per-dispatch durations of each measured kernel from the trace records
     recs = _csv_rows(os.path.join(prof_dir, "trace", "run_kernel_trace.csv"))
-    durs = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-                     for r in recs if kernel in r["Kernel_Name"]])
-    if durs.size:
-        lines.append(f"# {kernel}: {durs.size} dispatches; median {np.median(durs):.1f} us, "
-                     f"p10 {np.percentile(durs, 10):.1f} us, p90 {np.percentile(durs, 90):.1f} us")
-    # the dispatch resources rocprofv3 records, as printed (VGPR_Count is in
-    # 4-register units of the 8-register wave64 allocation granule, and
-    # LDS_Block_Size leaves out the dynamic LDS of the launch)
-    res = sorted({(r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["LDS_Block_Size"],
-                   r["Scratch_Size"], r["Workgroup_Size_X"], r["Grid_Size_X"])
-                  for r in recs if kernel in r["Kernel_Name"]})
-    for v, a, sg, lds, scr, wg, grid in res:
-        lines.append(f"# {kernel} dispatch fields: VGPR_Count {v} (= {2 * int(v)} VGPRs allocated), "
-                     f"Accum_VGPR_Count {a}, SGPR_Count {sg}, Scratch_Size {scr}, "
-                     f"LDS_Block_Size {lds}, Workgroup_Size {wg}, Grid_Size {grid}")
+    for part in kernel_parts(kernel):
+        durs = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                         for r in recs if part in r["Kernel_Name"]])
+        if durs.size:
+            lines.append(f"# {part}: {durs.size} dispatches; median {np.median(durs):.1f} us, "
+                         f"p10 {np.percentile(durs, 10):.1f} us, "
+                         f"p90 {np.percentile(durs, 90):.1f} us")
+        # the dispatch resources rocprofv3 records, as printed (VGPR_Count is
+        # in 4-register units of the 8-register wave64 allocation granule, and
+        # LDS_Block_Size leaves out the dynamic LDS of the launch)
+        res = sorted({(r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"],
+                       r["LDS_Block_Size"], r["Scratch_Size"], r["Workgroup_Size_X"],
+                       r["Grid_Size_X"])
+                      for r in recs if part in r["Kernel_Name"]})
+        for v, a, sg, lds, scr, wg, grid in res:
+            lines.append(f"# {part} dispatch fields: VGPR_Count {v} (= {2 * int(v)} VGPRs "
+                         f"allocated), Accum_VGPR_Count {a}, SGPR_Count {sg}, Scratch_Size {scr}, "
+                         f"LDS_Block_Size {lds}, Workgroup_Size {wg}, Grid_Size {grid}")
     variant = profile_variant(state_dtype)
     with open(profile_path(kernel, workload, "kernel_trace", variant), "w") as f:
         f.write("\n".join(lines) + "\n")
 
     def per_dispatch(counter, copy):
+        # mean per dispatch; for a step of several kernels, the sum of their
+        # means (the bytes of one step)
         sub = ("copy_" if copy else "") + counter
         rows = _csv_rows(os.path.join(prof_dir, sub, "run_counter_collection.csv"))
-        want = "__amd_rocclr_copyBuffer" if copy else kernel
-        vals = [float(r["Counter_Value"]) for r in rows
-                if want in r["Kernel_Name"] and r["Counter_Name"] == counter]
-        return sum(vals) / len(vals), len(vals)
+        total, n = 0.0, None
+        for want in ["__amd_rocclr_copyBuffer"] if copy else kernel_parts(kernel):
+            vals = [float(r["Counter_Value"]) for r in rows
+                    if want in r["Kernel_Name"] and r["Counter_Name"] == counter]
+            total += sum(vals) / len(vals)
+            n = len(vals) if n is None else min(n, len(vals))
+        return total, n
 
     gib_kib = (1 << 30) / 1024
     fetch, nf = per_dispatch("FETCH_SIZE", False)
@@ -248,10 +261,13 @@ def summarize_utilization(prof_dir: str, workload: str, kernel: str, run: str,
         if not os.path.exists(path):
             continue
         names = set()
+        parts = kernel_parts(kernel)
         for r in _csv_rows(path):
-            if kernel in r["Kernel_Name"]:
-                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-                names.add(r["Counter_Name"])
+            for part in parts:
+                if part in r["Kernel_Name"]:
+                    key = r["Counter_Name"] if len(parts) == 1 else f"{part}.{r['Counter_Name']}"
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+                    names.add(r["Counter_Name"])
         cmds.append(f"# command: rocprofv3 --pmc {' '.join(sorted(names))} --output-format csv "
                     f"-d {prof_dir}/{sub} -o run -- {run} --steps 5 --warmup 1 --cpu-budget 0")
     lines = [f"# rocprofv3 utilization counters: {kernel}, workload {workload}", *cmds,
@@ -583,7 +599,8 @@ def main():
 
     run = f"python3 bench.py --workload {args.workload}" + (
         f" --family {args.family}" if args.family else "") + (
-        f" --state-dtype {args.state_dtype}" if args.state_dtype != "f32" else "")
+        f" --state-dtype {args.state_dtype}" if args.state_dtype != "f32" else "") + (
+        f" --chunk-form {args.chunk_form}" if args.chunk_form != "workspace" else "")
     if args.summarize_utilization:
         summarize_utilization(args.summarize_utilization, args.workload, args.kernel, run,
                               args.state_dtype)
