@@ -51,16 +51,20 @@ namespace {
 constexpr int kVW = 16;          // value columns per wavefront
 constexpr int kNT = kVW / 16;    // 16-column MFMA tiles per wavefront
 
-// LDS layout of one workgroup (byte offsets).  Row pitches are padded by 16
-// bytes so that the MFMA operand reads of 16 consecutive rows hit distinct
-// banks.  fp32 activations keep a hi and a lo bf16 copy of keys and queries.
+// LDS layout of one workgroup (byte offsets).  The bf16 row pitches are 2 mod
+// 4 dwords: the 16 lanes that one cycle of an 8-byte operand read serves (16
+// consecutive rows at one column) then fall on 16 distinct bank pairs of the
+// 32-bank LDS, where a pitch of 0 mod 4 dwords would put rows m and m + 8 on
+// the same banks and double the time of every such read.  Those rows are only
+// 8-byte aligned, so every access to them is at most 8 bytes wide.  fp32
+// activations keep a hi and a lo bf16 copy of keys and queries.
 template <int K, int V, int ACT>
 struct ChunkPlan {
     static constexpr int NW = V / kVW;
     static constexpr int THREADS = NW * kWave;
     static constexpr int P = ACT == 0 ? 2 : 1;     // bf16 parts per input element
-    static constexpr int KT = K + 8;               // pitch of [C][K] (bf16)
-    static constexpr int KC = kC + 8;              // pitch of [K][C] and [C][C] (bf16)
+    static constexpr int KT = K + 4;               // pitch of [C][K] (bf16)
+    static constexpr int KC = kC + 4;              // pitch of [K][C] and [C][C] (bf16)
     static constexpr int LD = 16 + 4;              // pitch of a 16 x 16 fp32 block
     static constexpr int kScalars = 7;             // beta, e^G, e^{G_last-G}, rk, rq, G hi, G lo
     static constexpr int kt = 0;                              // P x [C][KT] raw keys
@@ -72,6 +76,8 @@ struct ChunkPlan {
     static constexpr int sc = pb + 2 * kC * KC * 2;           // 2 x kScalars x [C]
     static constexpr int bytes = sc + 2 * kScalars * kC * 4;
     static_assert(V % kVW == 0 && K % 32 == 0, "16-column waves, 32-deep key steps");
+    static_assert((KT / 2) % 4 == 2 && (KC / 2) % 4 == 2, "row pitches of 2 mod 4 dwords");
+    static_assert(lt % 16 == 0 && sc % 16 == 0, "fp32 regions stay 16-byte aligned");
     static_assert(bytes <= 160 * 1024, "LDS of one CU");
 };
 
@@ -272,13 +278,13 @@ gdn_chunk_fwd(const FusedParams p) {
                         qh[e] = hi;
                         ql[e] = lo;
                     }
-                    *reinterpret_cast<bf16x8*>(kt + t * KT + 8 * c8) = kh;
-                    *reinterpret_cast<bf16x8*>(qt + t * KT + 8 * c8) = qh;
-                    *reinterpret_cast<bf16x8*>(kt + kC * KT + t * KT + 8 * c8) = kl;
-                    *reinterpret_cast<bf16x8*>(qt + kC * KT + t * KT + 8 * c8) = ql;
+                    lds_put8(kt + t * KT + 8 * c8, kh);
+                    lds_put8(qt + t * KT + 8 * c8, qh);
+                    lds_put8(kt + kC * KT + t * KT + 8 * c8, kl);
+                    lds_put8(qt + kC * KT + t * KT + 8 * c8, ql);
                 } else {  // bf16 inputs are stored as they came
-                    *reinterpret_cast<u32x4v*>(kt + t * KT + 8 * c8) = L.k[i][0];
-                    *reinterpret_cast<u32x4v*>(qt + t * KT + 8 * c8) = L.q[i][0];
+                    lds_put8(kt + t * KT + 8 * c8, __builtin_bit_cast(bf16x8, L.k[i][0]));
+                    lds_put8(qt + t * KT + 8 * c8, __builtin_bit_cast(bf16x8, L.q[i][0]));
                 }
             }
         }
@@ -445,12 +451,12 @@ gdn_chunk_fwd(const FusedParams p) {
         };
         // (X K^T) tile products on bf16 MFMA (split parts for fp32 inputs).
         auto tile_product = [&](const __bf16* xa, const __bf16* xb, f32x4& acc, int kb) {
-            const bf16x8 av = lds_row8(xa + 32 * kb);
-            const bf16x8 bv = lds_row8(xb + 32 * kb);
+            const bf16x8 av = lds_row8_split(xa + 32 * kb);
+            const bf16x8 bv = lds_row8_split(xb + 32 * kb);
             acc = mma_bf16(av, bv, acc);
             if constexpr (P == 2) {
-                const bf16x8 al = lds_row8(xa + kC * KT + 32 * kb);
-                const bf16x8 bl = lds_row8(xb + kC * KT + 32 * kb);
+                const bf16x8 al = lds_row8_split(xa + kC * KT + 32 * kb);
+                const bf16x8 bl = lds_row8_split(xb + kC * KT + 32 * kb);
                 acc = mma_bf16(av, bl, acc);
                 acc = mma_bf16(al, bv, acc);
             }
@@ -488,8 +494,8 @@ gdn_chunk_fwd(const FusedParams p) {
 #pragma unroll
             for (int part = 0; part < P; ++part) {
                 const __bf16* src = kt + part * kC * KT + 2 * tp * KT + 8 * c8;
-                const bf16x8 a = lds_row8(src);
-                const bf16x8 b = lds_row8(src + KT);
+                const bf16x8 a = lds_row8_split(src);
+                const bf16x8 b = lds_row8_split(src + KT);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -97,6 +97,19 @@ __device__ __forceinline__ bf16x8 lds_row8(const __bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// Eight bf16 into a row that is only 8-byte aligned: two 8-byte writes.
+__device__ __forceinline__ void lds_put8(__bf16* dst, const bf16x8& x) {
+    *reinterpret_cast<bf16x4*>(dst) = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x4*>(dst + 4) = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+}
+
+// The same from a row that is only 8-byte aligned: two 8-byte reads.
+__device__ __forceinline__ bf16x8 lds_row8_split(const __bf16* p) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Eight consecutive activation elements at byte offset `off`, widened to fp32.
 template <int ACT>
 __device__ __forceinline__ void buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[8]) {
@@ -154,6 +167,24 @@ __device__ __forceinline__ double readlane_f64(double x, int l) {
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), l));
     const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), l));
     return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// e^x on the hardware base-2 exponential (v_exp_f32, about one ulp) of
+// x log2(e).  Rounding that product adds a relative error of about
+// |x| 2^-24 (below 1e-6 for |x| <= 16); the chunk's decay factors
+// e^{G_t - G_s} it serves lie in (0, 1], and where |x| is larger they are
+// negligible beside the factors near 1.  Overflows to +inf above x = 88.7,
+// as expf does; no denormal or special-case handling beyond the
+// instruction's own.
+__device__ __forceinline__ float exp_hw(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ int64_t readlane_i64(int64_t x, int l) {
+    const uint64_t b = static_cast<uint64_t>(x);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b)), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(b >> 32)), l));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // LDS written by some lanes of this wavefront becomes visible to its others.

@@ -112,7 +112,7 @@ struct PrepPlan {
     static constexpr int LDB = 18;               // pitch of a 16 x 16 fp32 block (8-byte rows)
     static constexpr int BLK = 16 * LDB;         // floats per block
     static constexpr int stage_bytes = 2 * P * kC * KT * 2;
-    static constexpr int block_bytes = 3 * kBlk * BLK * 4;   // L, A, P (fp32)
+    static constexpr int block_bytes = 2 * kBlk * BLK * 4;   // L, A (fp32)
     static constexpr int r0 = 0;                  // staged keys/queries, then the fp32 blocks
     static constexpr int r0_bytes = stage_bytes > block_bytes ? stage_bytes : block_bytes;
     static constexpr int kBatch = 4;              // v-heads whose gates are prepared at once
@@ -145,7 +145,6 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
     __bf16* const qt = kt + P * kC * KT;
     float* const Lb = reinterpret_cast<float*>(smem + Pl::r0);  // after the Gram tiles
     float* const Ab = Lb + kBlk * BLK;
-    float* const Pb = Ab + kBlk * BLK;
     float* const s_rk = reinterpret_cast<float*>(smem + Pl::sc);
     float* const s_rq = s_rk + kC;
     float* const s_beta0 = s_rq + kC;                  // [kBatch][C] each
@@ -160,10 +159,27 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
 
     const int64_t w = blockIdx.x / p.Hk;
     const int j = static_cast<int>(blockIdx.x % p.Hk);
-    const int i = find_seq(p, B, w, lane);
-    // the slot index and the sequence bounds load together
-    const int32_t slot = p.state_idx[i];
-    const int64_t bos = seq_bos(p, i), eos = seq_eos(p, i);
+    int32_t slot;
+    int64_t bos, eos;
+    int i;
+    if (B <= kWave) {
+        // one round trip: lane l loads sequence l's bounds and slot index, the
+        // sequence of this chunk slot is the last whose first slot is <= w
+        const int l = lane < B ? lane : 0;
+        const int32_t slot_l = p.state_idx[l];
+        const int64_t bos_l = seq_bos(p, l), eos_l = seq_eos(p, l);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(lane < B && bos_l / kC + l <= w);
+        i = 63 - __builtin_clzll(m);   // lane 0 always qualifies
+        slot = __builtin_amdgcn_readlane(slot_l, i);
+        bos = readlane_i64(bos_l, i);
+        eos = readlane_i64(eos_l, i);
+    } else {
+        i = find_seq(p, B, w, lane);
+        // the slot index and the sequence bounds load together
+        slot = p.state_idx[i];
+        bos = seq_bos(p, i);
+        eos = seq_eos(p, i);
+    }
     if (slot < 0) return;
     const int64_t c = w - (bos / kC + i);
     const int64_t t0 = bos + c * kC;
@@ -208,21 +224,39 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
         const auto qr = buffer_rsrc(static_cast<const char*>(p.q) + (t0 * p.q_stride + int64_t(j) * K) * esz,
                                     (Lc - 1) * qrow + K * esz);
         static_assert((kC * CPL) % Pl::THREADS == 0, "whole rows per pass");
-        // every row load first (one round trip), then the norms and splits
-        float xks[NQK][8], xqs[NQK][8];
+        // every row load first (one round trip), as raw words, then the norms
+        // and (fp32 inputs) the splits; bf16 rows are staged as loaded
+        constexpr int VEC = ACT == 0 ? 2 : 1;
+        u32x4v rks_[NQK][VEC], rqs_[NQK][VEC];
 #pragma unroll
         for (int n = 0; n < NQK; ++n) {
             const int vi = tid + n * Pl::THREADS;
             const int t = vi / CPL, c8 = vi % CPL;
-            buffer_load8<ACT>(kr, t * krow + 8 * c8 * esz, xks[n]);
-            buffer_load8<ACT>(qr, t * qrow + 8 * c8 * esz, xqs[n]);
+#pragma unroll
+            for (int h2 = 0; h2 < VEC; ++h2) {
+                rks_[n][h2] = __builtin_amdgcn_raw_buffer_load_b128(kr, t * krow + 8 * c8 * esz + 16 * h2, 0, 0);
+                rqs_[n][h2] = __builtin_amdgcn_raw_buffer_load_b128(qr, t * qrow + 8 * c8 * esz + 16 * h2, 0, 0);
+            }
         }
+        auto widen8 = [](const u32x4v (&w)[VEC], float (&x)[8]) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (ACT == 0) {
+                    x[e] = __uint_as_float(w[0][e]);
+                    x[4 + e] = __uint_as_float(w[VEC - 1][e]);
+                } else {
+                    x[2 * e] = bf16_lo(w[0][e]);
+                    x[2 * e + 1] = bf16_hi(w[0][e]);
+                }
+            }
+        };
 #pragma unroll
         for (int n = 0; n < NQK; ++n) {
             const int vi = tid + n * Pl::THREADS;
             const int t = vi / CPL, c8 = vi % CPL;
-            const float* const xk = xks[n];
-            const float* const xq = xqs[n];
+            float xk[8], xq[8];
+            widen8(rks_[n], xk);
+            widen8(rqs_[n], xq);
             float ssk = 0.0f, ssq = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -235,22 +269,25 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
                 s_rk[t] = t < Lc ? rsqrtf(ssk + p.eps) : 0.0f;
                 s_rq[t] = t < Lc ? p.scale * rsqrtf(ssq + p.eps) : 0.0f;
             }
-            bf16x8 kh, kl, qh, ql;
+            if constexpr (ACT == 0) {
+                bf16x8 kh, kl, qh, ql;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                __bf16 hi, lo;
-                split_bf16(xk[e], hi, lo);
-                kh[e] = hi;
-                kl[e] = lo;
-                split_bf16(xq[e], hi, lo);
-                qh[e] = hi;
-                ql[e] = lo;
-            }
-            *reinterpret_cast<bf16x8*>(kt + t * KT + 8 * c8) = kh;
-            *reinterpret_cast<bf16x8*>(qt + t * KT + 8 * c8) = qh;
-            if constexpr (P == 2) {
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 hi, lo;
+                    split_bf16(xk[e], hi, lo);
+                    kh[e] = hi;
+                    kl[e] = lo;
+                    split_bf16(xq[e], hi, lo);
+                    qh[e] = hi;
+                    ql[e] = lo;
+                }
+                *reinterpret_cast<bf16x8*>(kt + t * KT + 8 * c8) = kh;
+                *reinterpret_cast<bf16x8*>(qt + t * KT + 8 * c8) = qh;
                 *reinterpret_cast<bf16x8*>(kt + kC * KT + t * KT + 8 * c8) = kl;
                 *reinterpret_cast<bf16x8*>(qt + kC * KT + t * KT + 8 * c8) = ql;
+            } else {
+                *reinterpret_cast<u32x4v*>(kt + t * KT + 8 * c8) = rks_[n][0];
+                *reinterpret_cast<u32x4v*>(qt + t * KT + 8 * c8) = rqs_[n][0];
             }
         }
     }
@@ -258,7 +295,10 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
 
     // ---- raw Gram tiles, once for the group: task 0..3 the diagonal blocks
     // of K K^T, 4..9 the blocks below them, 10..19 the blocks of Q K^T on and
-    // below the diagonal.
+    // below the diagonal, those computed transposed (K Q^T): the accumulator
+    // of a transposed tile holds in lane (g, m) row m and columns 4 g .. + 3
+    // of the Q K^T block, which is the operand fragment the state pass reads,
+    // so P goes from registers to the workspace without passing through LDS.
     auto tile_of = [](int task, bool& isq, int& ti, int& tj) {
         isq = task >= 10;
         if (task < 4) {
@@ -279,8 +319,8 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
         bool isq;
         int ti, tj;
         tile_of(wave + 4 * n, isq, ti, tj);
-        const __bf16* xa = (isq ? qt : kt) + (16 * ti + m16) * KT + 8 * g4;
-        const __bf16* xb = kt + (16 * tj + m16) * KT + 8 * g4;
+        const __bf16* xa = kt + (16 * (isq ? tj : ti) + m16) * KT + 8 * g4;
+        const __bf16* xb = (isq ? qt : kt) + (16 * (isq ? ti : tj) + m16) * KT + 8 * g4;
         acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -296,7 +336,7 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
         }
     }
     // (the barrier at the top of the v-head loop ends the staged rows' life:
-    // the region then holds L, A and P)
+    // the region then holds L and A)
 
 #pragma unroll 1
     for (int gb = 0; gb < p.G; gb += Pl::kBatch) {
@@ -325,13 +365,13 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
             s_Glo0[wave * kC + lane] = static_cast<float>(G - static_cast<double>(Ghi));
             float* const out_sc = reinterpret_cast<float*>(ws + (static_cast<size_t>(w) * p.Hv + h) *
                                                                     WsEntry::bytes + WsEntry::SC);
-            const float eG = expf(Ghi);
+            const float eG = exp_hw(Ghi);
             const float rk = s_rk[lane], rq = s_rq[lane];
             out_sc[lane] = bet;
             out_sc[kC + lane] = eG * rk;
             out_sc[2 * kC + lane] = eG * rq;
-            out_sc[3 * kC + lane] = rk * expf(static_cast<float>(Glast - G));
-            out_sc[4 * kC + lane] = expf(static_cast<float>(Glast));
+            out_sc[3 * kC + lane] = rk * exp_hw(static_cast<float>(Glast - G));
+            out_sc[4 * kC + lane] = exp_hw(static_cast<float>(Glast));
         }
         lds_barrier();   // this batch's gates are in; the staged rows are dead
 
@@ -344,31 +384,59 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
         const float* const s_Glo = s_Glo0 + (g - gb) * kC;
         if (g > gb) lds_barrier();   // the previous v-head's blocks are packed
 
-        // ---- scale into L (strictly below the diagonal) and P (on and below it)
+        // ---- scale into L (strictly below the diagonal; LDS) and P (on and
+        // below it; straight into the entry's operand fragments)
 #pragma unroll
         for (int n = 0; n < 5; ++n) {
             bool isq;
             int ti, tj;
             tile_of(wave + 4 * n, isq, ti, tj);
-            const int s = 16 * tj + m16;
-            const float rks = s_rk[s], Gs = s_G[s], Gls = s_Glo[s];
-            // the four row tokens' scalars as vectors (rows 16 ti + 4 g4 ..)
-            const int t4 = 16 * ti + 4 * g4;
-            const float4 G4 = *reinterpret_cast<const float4*>(s_G + t4);
-            const float4 GL4 = *reinterpret_cast<const float4*>(s_Glo + t4);
-            const float4 X4 = isq ? *reinterpret_cast<const float4*>(s_rq + t4)
-                                  : *reinterpret_cast<const float4*>(s_beta + t4);
-            const float4 K4 = *reinterpret_cast<const float4*>(s_rk + t4);
-            const float Gt[4] = {G4.x, G4.y, G4.z, G4.w};
-            const float GLt[4] = {GL4.x, GL4.y, GL4.z, GL4.w};
-            const float Xt[4] = {X4.x, X4.y, X4.z, X4.w};
-            const float Kt[4] = {K4.x, K4.y, K4.z, K4.w};
-            float* const dst = (isq ? Pb : Lb) + blk_of(ti, tj) * BLK;
+            if (!isq) {
+                // L block (ti, tj): lane (g, m) holds rows t = 16 ti + 4 g + e,
+                // column s = 16 tj + m
+                const int s = 16 * tj + m16;
+                const float rks = s_rk[s], Gs = s_G[s], Gls = s_Glo[s];
+                const int t4 = 16 * ti + 4 * g4;
+                const float4 G4 = *reinterpret_cast<const float4*>(s_G + t4);
+                const float4 GL4 = *reinterpret_cast<const float4*>(s_Glo + t4);
+                const float4 X4 = *reinterpret_cast<const float4*>(s_beta + t4);
+                const float4 K4 = *reinterpret_cast<const float4*>(s_rk + t4);
+                const float Gt[4] = {G4.x, G4.y, G4.z, G4.w};
+                const float GLt[4] = {GL4.x, GL4.y, GL4.z, GL4.w};
+                const float Xt[4] = {X4.x, X4.y, X4.z, X4.w};
+                const float Kt[4] = {K4.x, K4.y, K4.z, K4.w};
+                float* const dst = Lb + blk_of(ti, tj) * BLK;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = t4 + e;
-                const float f = t >= s ? expf((Gt[e] - Gs) + (GLt[e] - Gls)) * rks * acc[n][e] : 0.0f;
-                dst[(4 * g4 + e) * LDB + m16] = isq ? Xt[e] * f : (t > s ? Xt[e] * Kt[e] * f : 0.0f);
+                for (int e = 0; e < 4; ++e) {
+                    const int t = t4 + e;
+                    // (computed for every element, kept below the diagonal)
+                    const float ex = exp_hw((Gt[e] - Gs) + (GLt[e] - Gls));
+                    dst[(4 * g4 + e) * LDB + m16] = t > s ? Xt[e] * Kt[e] * (ex * rks * acc[n][e]) : 0.0f;
+                }
+            } else {
+                // P block (ti, tj), transposed tile: lane (g, m) holds row
+                // t = 16 ti + m, columns s = 16 tj + 4 g + e
+                const int t = 16 * ti + m16;
+                const float rqt = s_rq[t], Gt = s_G[t], Glt = s_Glo[t];
+                const int s4 = 16 * tj + 4 * g4;
+                const float4 G4 = *reinterpret_cast<const float4*>(s_G + s4);
+                const float4 GL4 = *reinterpret_cast<const float4*>(s_Glo + s4);
+                const float4 K4 = *reinterpret_cast<const float4*>(s_rk + s4);
+                const float Gs[4] = {G4.x, G4.y, G4.z, G4.w};
+                const float GLs[4] = {GL4.x, GL4.y, GL4.z, GL4.w};
+                const float Ks[4] = {K4.x, K4.y, K4.z, K4.w};
+                f32x4 pv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = s4 + e;
+                    const float ex = exp_hw((Gt - Gs[e]) + (Glt - GLs[e]));
+                    pv[e] = t >= s ? rqt * (ex * Ks[e] * acc[n][e]) : 0.0f;
+                }
+                const Split4 sp = split_tile(pv);
+                char* const base = entry + WsEntry::P + blk_of(ti, tj) * 2 * kFragBytes + lane * 8;
+                *reinterpret_cast<bf16x4*>(base) = sp.hi;
+                if constexpr (P == 2)   // with bf16 activations the state pass reads P's hi parts only
+                    *reinterpret_cast<bf16x4*>(base + kFragBytes) = sp.lo;
             }
         }
         lds_barrier();
@@ -428,43 +496,54 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
             lds_barrier();
         }
 
-        // ---- pack A and P into bf16 hi/lo operand fragments: lane (g, m) of
+        // ---- pack A into bf16 hi/lo operand fragments: lane (g, m) of
         // block (bi, bj) holds rows 16 bi + m, columns 16 bj + 4 g .. + 3
 #pragma unroll
-        for (int n = 0; n < 5; ++n) {
-            const int task = wave + 4 * n;                    // 0..9 A, 10..19 P
-            const bool isp = task >= kBlk;
-            const int blk = isp ? task - kBlk : task;
-            const float* const src = (isp ? Pb : Ab) + blk * BLK + m16 * LDB + 4 * g4;
-            const float2 v01 = *reinterpret_cast<const float2*>(src);
-            const float2 v23 = *reinterpret_cast<const float2*>(src + 2);
-            const Split4 sp = split_tile(f32x4{v01.x, v01.y, v23.x, v23.y});
-            char* const base = entry + (isp ? WsEntry::P : WsEntry::A) + blk * 2 * kFragBytes + lane * 8;
-            *reinterpret_cast<bf16x4*>(base) = sp.hi;
-            if (!isp || P == 2)   // with bf16 activations the state pass reads P's hi parts only
+        for (int n = 0; n < 3; ++n) {
+            const int blk = wave + 4 * n;
+            if (blk < kBlk) {
+                const float* const src = Ab + blk * BLK + m16 * LDB + 4 * g4;
+                const float2 v01 = *reinterpret_cast<const float2*>(src);
+                const float2 v23 = *reinterpret_cast<const float2*>(src + 2);
+                const Split4 sp = split_tile(f32x4{v01.x, v01.y, v23.x, v23.y});
+                char* const base = entry + WsEntry::A + blk * 2 * kFragBytes + lane * 8;
+                *reinterpret_cast<bf16x4*>(base) = sp.hi;
                 *reinterpret_cast<bf16x4*>(base + kFragBytes) = sp.lo;
+            }
         }
     }
     }
 }
 
 // Per (sequence, v-head): the state pass over the chunks, reading each
-// chunk's A, P and scalars from the workspace.
+// chunk's A, P and scalars from the workspace.  Each wavefront holds one
+// 16-column tile of the state.  (Two tiles per wavefront, so that every
+// operand fragment read from LDS serves both, halved the LDS traffic but left
+// one wavefront per SIMD at V = 128 with nothing to hide its latencies behind:
+// 166 against 133 us on the long varlen batch.)
 template <int K, int V, int ACT>
 struct StatePlan {
     static constexpr int NW = V / 16;
     static constexpr int THREADS = NW * kWave;
     static constexpr int P = ACT == 0 ? 2 : 1;
-    static constexpr int KT = K + 8;              // pitch of [C][K] (bf16)
-    static constexpr int KC = kC + 8;             // pitch of [K][C] (bf16)
+    // Row pitches of 2 mod 4 dwords: the 16 lanes that one cycle of an 8-byte
+    // operand read serves (rows m16 = 0..15 at one column) then fall on 16
+    // distinct bank pairs of the 32-bank LDS.  (A pitch of 0 mod 4 dwords,
+    // as 16-byte row accesses would want, puts rows m16 and m16 + 8 on the
+    // same banks and doubles the time of every operand read.)  Rows are
+    // therefore only 8-byte aligned, and every access to them is 8 bytes wide
+    // at most.
+    static constexpr int KT = K + 4;              // pitch of [C][K] (bf16)
+    static constexpr int KC = kC + 4;             // pitch of [K][C] (bf16)
     static constexpr int kt = 0;                                  // P x [C][KT] raw keys
     static constexpr int qt = kt + P * kC * KT * 2;               // P x [C][KT] raw queries
     static constexpr int kc = qt + P * kC * KT * 2;               // P x [K][KC] raw keys, transposed
-    static constexpr int en = kc + P * K * KC * 2;                // the chunk's workspace entry
+    static constexpr int en = (kc + P * K * KC * 2 + 15) / 16 * 16;   // the chunk's workspace entry
     static constexpr int bytes = en + WsEntry::bytes;
     static constexpr int EV = WsEntry::bytes / 16;                // 16-byte vectors per entry
     static constexpr int NEV = (EV + THREADS - 1) / THREADS;      // per thread
     static_assert(V % 16 == 0 && K % 32 == 0, "16-column waves, 32-deep key steps");
+    static_assert((KT / 2) % 4 == 2 && (KC / 2) % 4 == 2, "row pitches of 2 mod 4 dwords");
     static_assert(bytes <= 160 * 1024, "LDS of one CU");
 };
 
@@ -545,6 +624,20 @@ gdn_chunk_state(const FusedParams p, const char* ws) {
         const int64_t rest = eos - (bos + static_cast<int64_t>(cn) * kC);
         return static_cast<int>(rest < kC ? rest : kC);
     };
+    // Token t and 8-element column group c8 that thread-slot vi stages.  At
+    // K = 128 each 16 lanes take 8 groups of two tokens (rather than all 16
+    // groups of one), so that their 8-byte LDS writes cover all 32 banks
+    // once; every 8 lanes still load 128 contiguous bytes of a row.
+    auto stage_pos = [](int vi, int& t, int& c8) {
+        if constexpr (CPL == 16) {
+            const int r = vi % 32;
+            t = 2 * (vi / 32) + ((r >> 3) & 1);
+            c8 = (r & 7) + 8 * (r >> 4);
+        } else {
+            t = vi / CPL;
+            c8 = vi % CPL;
+        }
+    };
     // Loads of one chunk, issued a chunk ahead: raw keys and queries, and the
     // chunk's workspace entry.
     struct Loads {
@@ -561,8 +654,8 @@ gdn_chunk_state(const FusedParams p, const char* ws) {
                                     (Ln - 1) * qrow + K * esz);
 #pragma unroll
         for (int n = 0; n < NQK; ++n) {
-            const int vi = tid + n * Pl::THREADS;
-            const int t = vi / CPL, c8 = vi % CPL;
+            int t, c8;
+            stage_pos(tid + n * Pl::THREADS, t, c8);
 #pragma unroll
             for (int h2 = 0; h2 < VEC; ++h2) {
                 L.k[n][h2] = __builtin_amdgcn_raw_buffer_load_b128(kr, t * krow + (8 * c8 * esz + 16 * h2), 0, 0);
@@ -581,7 +674,8 @@ gdn_chunk_state(const FusedParams p, const char* ws) {
         for (int n = 0; n < NQK; ++n) {
             const int vi = tid + n * Pl::THREADS;
             if ((kC * CPL) % Pl::THREADS == 0 || vi < kC * CPL) {
-                const int t = vi / CPL, c8 = vi % CPL;
+                int t, c8;
+                stage_pos(vi, t, c8);
                 if constexpr (ACT == 0) {
                     bf16x8 kh, kl, qh, ql;
 #pragma unroll
@@ -596,13 +690,13 @@ gdn_chunk_state(const FusedParams p, const char* ws) {
                         qh[e] = hi;
                         ql[e] = lo;
                     }
-                    *reinterpret_cast<bf16x8*>(kt + t * KT + 8 * c8) = kh;
-                    *reinterpret_cast<bf16x8*>(qt + t * KT + 8 * c8) = qh;
-                    *reinterpret_cast<bf16x8*>(kt + kC * KT + t * KT + 8 * c8) = kl;
-                    *reinterpret_cast<bf16x8*>(qt + kC * KT + t * KT + 8 * c8) = ql;
+                    lds_put8(kt + t * KT + 8 * c8, kh);
+                    lds_put8(qt + t * KT + 8 * c8, qh);
+                    lds_put8(kt + kC * KT + t * KT + 8 * c8, kl);
+                    lds_put8(qt + kC * KT + t * KT + 8 * c8, ql);
                 } else {
-                    *reinterpret_cast<u32x4v*>(kt + t * KT + 8 * c8) = L.k[n][0];
-                    *reinterpret_cast<u32x4v*>(qt + t * KT + 8 * c8) = L.q[n][0];
+                    lds_put8(kt + t * KT + 8 * c8, __builtin_bit_cast(bf16x8, L.k[n][0]));
+                    lds_put8(qt + t * KT + 8 * c8, __builtin_bit_cast(bf16x8, L.q[n][0]));
                 }
             }
         }
@@ -620,8 +714,8 @@ gdn_chunk_state(const FusedParams p, const char* ws) {
 #pragma unroll
             for (int part = 0; part < P; ++part) {
                 const __bf16* src = kt + part * kC * KT + 2 * tp * KT + 8 * c8;
-                const bf16x8 a = lds_row8(src);
-                const bf16x8 b = lds_row8(src + KT);
+                const bf16x8 a = lds_row8_split(src);
+                const bf16x8 b = lds_row8_split(src + KT);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
