@@ -153,6 +153,55 @@ def cpu_baseline(inp, pool_rows: np.ndarray, budget_s: float):
             "single_core_sample": f"the same batch on 1 thread, repeated {reps1}x over {el1:.1f} s"}
 
 
+def cpu_table(args):
+    """The oracle over every configuration on the host cores, at all cores and
+    at one thread: median wall time of 3 runs of the whole batch (1 run where
+    a run exceeds 10 s), input generation excluded.  Writes
+    profiles/cpu_baseline__oracle.txt.  A reported baseline, not a target."""
+    import oracle
+    oracle.build(force=False)
+    threads = cpu_threads()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    lines = ["# CPU oracle (fp64 C, OpenMP over (sequence, v-head) units) on the host cores",
+             f"# command: python3 bench.py --cpu-table",
+             f"# cores available: {threads}; cpu: {model}",
+             "# workload | threads | runs | median_s | updates | updates/s | algorithmic GB/s"]
+    for name, wl in W.ALL.items():
+        inp = W.make_host_inputs(wl)
+        B = inp.wl.num_seqs
+        idx = np.where(inp.state_idx >= 0, np.arange(B), -1).astype(np.int32)
+        # the live sequences' initial states, drawn directly (the pools of the
+        # large configurations hold GiBs the oracle never touches)
+        rng = np.random.default_rng(wl.seed + 1)
+        rows0 = (rng.standard_normal((B,) + W.pool_shape(wl)[1:], dtype=np.float32)
+                 * np.float32(wl.pool_std))
+        updates = W.active_updates(inp)
+        nbytes = W.algorithmic_bytes(inp)
+        for nth in (threads, 1):
+            times = []
+            while len(times) < 3:
+                pool = np.ascontiguousarray(rows0, dtype=np.float32).copy()
+                t0 = time.perf_counter()
+                oracle.update(inp.q, inp.k, inp.v, inp.a, inp.b, inp.A_log, inp.dt_bias, pool, idx,
+                              inp.cu_seqlens, tokens_per_seq=inp.wl.tokens_per_seq,
+                              intermediates=inp.wl.intermediates, threads=nth)
+                times.append(time.perf_counter() - t0)
+                if times[-1] > 10.0:
+                    break
+            med = float(np.median(times))
+            lines.append(f"{name} | {nth} | {len(times)} | {med:.4f} | {updates} | "
+                         f"{updates / med:.4g} | {nbytes / med / 1e9:.3f}")
+            print(lines[-1], flush=True)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "cpu_baseline__oracle.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def kernel_parts(kernel: str):
     """The kernels of one step: a name of the form "a+b" is a step of two."""
     return kernel.split("+")
@@ -595,12 +644,19 @@ def main():
                     help="instead: write the profiles/ utilization summary from rocprofv3 --pmc "
                          "passes in the subdirectories of DIR")
     ap.add_argument("--kernel", default="gdn_decode_rows", help="kernel name for --summarize-profiles")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="instead: time the CPU oracle over every configuration at all cores and at "
+                         "one thread, and write profiles/cpu_baseline__oracle.txt")
     args = ap.parse_args()
 
     run = f"python3 bench.py --workload {args.workload}" + (
         f" --family {args.family}" if args.family else "") + (
         f" --state-dtype {args.state_dtype}" if args.state_dtype != "f32" else "") + (
         f" --chunk-form {args.chunk_form}" if args.chunk_form != "workspace" else "")
+    if args.cpu_table:
+        cpu_table(args)
+        return
+
     if args.summarize_utilization:
         summarize_utilization(args.summarize_utilization, args.workload, args.kernel, run,
                               args.state_dtype)

@@ -13,12 +13,13 @@
 // over all chunks at once (with a chunk index table for varlen batches), and
 // leaves the sequential pass over the chunks to a second kernel.  Here:
 //
-//   gdn_chunk_prep   one workgroup per (chunk, v-head), all in parallel: the
-//                    Gram tiles on bf16 MFMA, the scaled L and P, the full
-//                    inverse A = (I + L)^-1 (diagonal blocks by forward
-//                    substitution, the blocks below them on fp32 MFMA), and
-//                    the per-token scalars.  A and P are written as the bf16
-//                    hi/lo operand fragments the state pass reads.
+//   gdn_chunk_prep   one workgroup per (chunk slot, k-head), all in parallel:
+//                    the Gram tiles on bf16 MFMA once for the k-head, then
+//                    per v-head the scaled L and P, the full inverse
+//                    A = (I + L)^-1 (diagonal blocks by forward substitution,
+//                    the blocks below them on fp32 MFMA), and the per-token
+//                    scalars.  A and P are written as the bf16 hi/lo operand
+//                    fragments the state pass reads.
 //   gdn_chunk_state  one workgroup per (sequence, v-head), eight wavefronts of
 //                    16 value columns with their K x 16 state slice in MFMA
 //                    accumulators, walking the chunks in order: K S0 and Q S0,

@@ -14,6 +14,11 @@ constexpr int kWave = 64;
 // byte offset.  Accesses at or past `bytes` are bounds-checked by the hardware
 // (loads return 0, stores are dropped).
 constexpr int kBufNonTemporal = 2;           // cache-policy bit "nt" (gfx94x/gfx950)
+// State write-back: "nt" plus "sc1" (device scope).  On MI355X a probe of the
+// decode's in-place tile stream (1 GiB of 64 KiB tiles at random slots) ran
+// at 344.5 us with it against 350.0 us with "nt" alone, and write-only
+// streams 2% faster; loads keep "nt" (with "sc1" they ran no faster).
+constexpr int kBufStoreStream = 2 | 16;
 // Word 3 of a gfx9-family raw buffer resource: 32-bit data format, no swizzle.
 constexpr int kBufWord3 = 0x00020000;
 

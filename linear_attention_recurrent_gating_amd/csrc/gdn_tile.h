@@ -93,14 +93,14 @@ __device__ __forceinline__ void tile_store_all(const TileIO& t, OFF off, const f
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const u32x2 v = {bf16_rne_pair(s[i].x, s[i].y), bf16_rne_pair(s[i].z, s[i].w)};
-            __builtin_amdgcn_raw_buffer_store_b64(v, t.r, t.lane_bytes, off(i) << 1, kBufNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(v, t.r, t.lane_bytes, off(i) << 1, kBufStoreStream);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const u32x4 v = {__float_as_uint(s[i].x), __float_as_uint(s[i].y), __float_as_uint(s[i].z),
                              __float_as_uint(s[i].w)};
-            __builtin_amdgcn_raw_buffer_store_b128(v, t.r, t.lane_bytes, off(i) << 2, kBufNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(v, t.r, t.lane_bytes, off(i) << 2, kBufStoreStream);
         }
     }
 }

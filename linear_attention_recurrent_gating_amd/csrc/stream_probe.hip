@@ -7,9 +7,10 @@
 // Access shape (the row-split kernel's at K = V = 128 with 32 rows per lane):
 // a 256-thread workgroup streams two 64 KiB fp32 tiles, two wavefronts per
 // tile.  Lane l of a wavefront covers 16 bytes of row 2i + l/32 of its half of
-// the tile, so every 128-bit non-temporal load or store instruction moves one
-// contiguous kilobyte, and each lane issues 32 of them.  Tiles are picked
-// through an index list (random slots of a pool, as the decode sees them).
+// the tile, so every 128-bit load or store instruction moves one contiguous
+// kilobyte, and each lane issues 32 of them; loads and stores carry the cache
+// policies of the update kernels.  Tiles are picked through an index list
+// (random slots of a pool, as the decode sees them).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,7 +18,8 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBufNonTemporal = 2;
+constexpr int kBufNonTemporal = 2;          // loads: "nt"
+constexpr int kBufStoreStream = 2 | 16;     // stores: "nt" + "sc1", as the update kernels' state write-back
 constexpr int kWord3 = 0x00020000;
 constexpr int kTileBytes = 64 * 1024;
 constexpr int kRows = 32;            // 128-bit accesses per lane per tile half
@@ -47,7 +49,7 @@ __global__ void __launch_bounds__(256) gdn_stream_probe_bf16(char* pool, const i
     for (int i = 0; i < kRows; ++i) {
         x[i].x += s;
         x[i].y += s;
-        __builtin_amdgcn_raw_buffer_store_b64(x[i], r, lane_bytes, i * 512, kBufNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b64(x[i], r, lane_bytes, i * 512, kBufStoreStream);
     }
 }
 
@@ -107,13 +109,13 @@ __global__ void __launch_bounds__(256) gdn_stream_probe(const char* pool, char* 
                 const auto w = rsrc(dst + ((seq * 4 + t) * heads + h) * kTileBytes);
 #pragma unroll
                 for (int i = 0; i < kRows; ++i)
-                    __builtin_amdgcn_raw_buffer_store_b128(x[i], w, lane_bytes, i * kRowStep, kBufNonTemporal);
+                    __builtin_amdgcn_raw_buffer_store_b128(x[i], w, lane_bytes, i * kRowStep, kBufStoreStream);
             }
         }
         const auto w = KIND == kCopy ? rsrc(dst + tile * kTileBytes) : r;
 #pragma unroll
         for (int i = 0; i < kRows; ++i)
-            __builtin_amdgcn_raw_buffer_store_b128(x[i], w, lane_bytes, i * kRowStep, kBufNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(x[i], w, lane_bytes, i * kRowStep, kBufStoreStream);
     }
 }
 
