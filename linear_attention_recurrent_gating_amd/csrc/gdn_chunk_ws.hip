@@ -215,6 +215,52 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
     };
     load_gates(wave);
 
+    // Gates and log-decay prefix sums of v-head gb + wave (token `lane`) into
+    // the batch's LDS scalars, and the state pass's per-token scalars of that
+    // head: beta and e^{G_last} at once, the three that need the norms from
+    // e^G and e^{G_last - G}, kept in registers until the norms are staged.
+    float eG_w = 0.0f, dG_w = 0.0f;
+    auto sc_of = [&](int g) {
+        return reinterpret_cast<float*>(ws + (static_cast<size_t>(w) * p.Hv + j * p.G + g) * WsEntry::bytes +
+                                        WsEntry::SC);
+    };
+    auto gate_prep = [&](int gb) {
+        if (gb + wave < p.G) {
+            float glog = 0.0f, bet = 0.0f;
+            if (lane < Lc) {
+                if (p.g) {
+                    glog = ga_n;
+                    bet = gb_n;
+                } else {
+                    gate_values(ga_n, gb_n, Alog_n, dtb_n, glog, bet);
+                }
+            }
+            load_gates(gb + wave + Pl::kBatch);   // the next batch's, ahead
+            const double G = wave_prefix_sum(static_cast<double>(glog));
+            // G as an unevaluated float pair: differences of nearby sums come
+            // out exact in the high parts (Sterbenz) plus the low parts
+            const float Ghi = static_cast<float>(G);
+            s_beta0[wave * kC + lane] = bet;
+            s_G0[wave * kC + lane] = Ghi;
+            s_Glo0[wave * kC + lane] = static_cast<float>(G - static_cast<double>(Ghi));
+            const double Glast = readlane_f64(G, kWave - 1);
+            float* const out_sc = sc_of(gb + wave);
+            out_sc[lane] = bet;
+            out_sc[4 * kC + lane] = exp_hw(static_cast<float>(Glast));
+            eG_w = exp_hw(Ghi);
+            dG_w = exp_hw(static_cast<float>(Glast - G));
+        }
+    };
+    auto write_scalars = [&](int gb) {
+        if (gb + wave < p.G) {
+            float* const out_sc = sc_of(gb + wave);
+            const float rk = s_rk[lane], rq = s_rq[lane];
+            out_sc[kC + lane] = eG_w * rk;
+            out_sc[2 * kC + lane] = eG_w * rq;
+            out_sc[3 * kC + lane] = rk * dG_w;
+        }
+    };
+
     // ---- stage raw keys and queries (rows past the chunk load as zero) and
     // their inverse norms
     {
@@ -239,6 +285,8 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
                 rqs_[n][h2] = __builtin_amdgcn_raw_buffer_load_b128(qr, t * qrow + 8 * c8 * esz + 16 * h2, 0, 0);
             }
         }
+        // the first batch's gates while the rows are in flight
+        gate_prep(0);
         auto widen8 = [](const u32x4v (&w)[VEC], float (&x)[8]) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -341,39 +389,10 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
 
 #pragma unroll 1
     for (int gb = 0; gb < p.G; gb += Pl::kBatch) {
-        // ---- gates and log-decay prefix sums of v-head gb + wave (token
-        // `lane`), and the state pass's per-token scalars of that head
-        if (gb + wave < p.G) {
-            const int g = gb + wave;
-            const int h = j * p.G + g;
-            float glog = 0.0f, bet = 0.0f;
-            if (lane < Lc) {
-                if (p.g) {
-                    glog = ga_n;
-                    bet = gb_n;
-                } else {
-                    gate_values(ga_n, gb_n, Alog_n, dtb_n, glog, bet);
-                }
-            }
-            load_gates(g + Pl::kBatch);   // the next batch's, ahead
-            const double G = wave_prefix_sum(static_cast<double>(glog));
-            const double Glast = readlane_f64(G, kWave - 1);
-            // G as an unevaluated float pair: differences of nearby sums come
-            // out exact in the high parts (Sterbenz) plus the low parts
-            const float Ghi = static_cast<float>(G);
-            s_beta0[wave * kC + lane] = bet;
-            s_G0[wave * kC + lane] = Ghi;
-            s_Glo0[wave * kC + lane] = static_cast<float>(G - static_cast<double>(Ghi));
-            float* const out_sc = reinterpret_cast<float*>(ws + (static_cast<size_t>(w) * p.Hv + h) *
-                                                                    WsEntry::bytes + WsEntry::SC);
-            const float eG = exp_hw(Ghi);
-            const float rk = s_rk[lane], rq = s_rq[lane];
-            out_sc[lane] = bet;
-            out_sc[kC + lane] = eG * rk;
-            out_sc[2 * kC + lane] = eG * rq;
-            out_sc[3 * kC + lane] = rk * exp_hw(static_cast<float>(Glast - G));
-            out_sc[4 * kC + lane] = exp_hw(static_cast<float>(Glast));
-        }
+        // ---- the batch's gates (the first batch's were prepared during the
+        // staging) and the state pass's per-token scalars of its heads
+        if (gb > 0) gate_prep(gb);
+        write_scalars(gb);
         lds_barrier();   // this batch's gates are in; the staged rows are dead
 
 #pragma unroll 1

@@ -8,9 +8,10 @@
 // device array, so it is never passed anywhere: its address on a device is
 // looked up once per device, with that device current, and only that address
 // is used from then on.  Nothing in it needs clearing between calls (every
-// byte a kernel reads was written by an earlier kernel of the same call), but
-// every call on one GPU uses the same bytes, so calls that may overlap on a
-// GPU race.
+// value a kernel computes with was written by an earlier kernel of the same
+// call; bytes staged but unused, such as the lo parts of P with bf16
+// activations, may hold anything), but every call on one GPU uses the same
+// bytes, so calls that may overlap on a GPU race.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
