@@ -109,7 +109,11 @@ template <int K, int ACT>
 struct PrepPlan {
     static constexpr int THREADS = 256;
     static constexpr int P = ACT == 0 ? 2 : 1;   // bf16 parts per input element
-    static constexpr int KT = K + 8;             // pitch of the staged [C][K] rows (bf16)
+    // Pitch of the staged [C][K] rows (bf16).  The prep reads them as 16-byte
+    // Gram operands, 8 lanes (rows) per cycle: a pitch of 4 mod 8 dwords puts
+    // those 8 rows on distinct 4-bank groups (the state pass, which reads 8
+    // bytes of 16 rows per cycle, uses 2 mod 4 instead).
+    static constexpr int KT = K + 8;
     static constexpr int LDB = 18;               // pitch of a 16 x 16 fp32 block (8-byte rows)
     static constexpr int BLK = 16 * LDB;         // floats per block
     static constexpr int stage_bytes = 2 * P * kC * KT * 2;
