@@ -134,16 +134,17 @@ def test_row_split_sixteen_rows_per_lane(dev, K, V):
         full_check(wl, dev, family=gdn.GDN_KERNEL_ROW_SPLIT, block_k=bk)
 
 
-@pytest.mark.parametrize("K,V", [(32, 32), (64, 64), (128, 32), (128, 64), (128, 128),
-                                 (256, 64), (256, 128)], ids=lambda x: str(x))
+# Every (K, V) with such an instance: block_k = 32 * 64 / (V / 4) must not
+# exceed K (which rules out (32, 32), (64, 64) and (128, 32)).
+@pytest.mark.parametrize("K,V", [(128, 64), (128, 128), (256, 64), (256, 128)],
+                         ids=lambda x: str(x))
 def test_row_split_thirty_two_rows_per_lane(dev, K, V):
     """Row split with 32 state rows per lane (block_k = 32 * rows per
     instruction): the instance chosen for large fp32 grids at K = V = 128."""
     import linear_attention_recurrent_gating_amd as gdn
     rg = 64 // (V // 4)
     bk = 32 * rg
-    if bk > K or K // bk > 8:
-        pytest.skip(f"no 32-rows-per-lane instance for K={K}, V={V}")
+    assert bk <= K and K // bk <= 8
     for act, seed in ((W.ACT_BF16, 65), (W.ACT_F32, 66)):
         wl = W.Workload(f"rows32_k{K}_v{V}_{act}", seed + K + V, 5, 1, 2, 4, K, V, act, 8, 0.05,
                         num_padded=1)
