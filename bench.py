@@ -15,6 +15,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -619,6 +620,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay captured HIP graphs (one per slot set, each holding one step's "
                          "launches) instead of launching every step from Python")
+    ap.add_argument("--intermediates", action="store_true",
+                    help="also write the state after every token (the workload's own setting otherwise)")
     ap.add_argument("--unfused", action="store_true",
                     help="time the unfused pair instead: gdn_gating + gdn_recurrent_update per step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -724,6 +727,8 @@ def main():
         return
 
     wl = W.ALL[args.workload]
+    if args.intermediates:
+        wl = dataclasses.replace(wl, intermediates=True)
     inp = W.make_host_inputs(wl)
     d = W.to_torch(inp, dev)
     sets = max(1, args.slot_sets if wl.num_slots >= args.slot_sets * wl.num_seqs else 1)
@@ -842,7 +847,7 @@ def main():
     # The committed counter profiles were taken with the library's tiling, the
     # KV layout and fused gates (fp32 state, or bf16 state under their own
     # file names); other runs get none.
-    profiled = (args.layout == "KV" and not args.unfused
+    profiled = (args.layout == "KV" and not args.unfused and not args.intermediates
                 and not (args.block_v or args.block_k or args.waves))
     traffic = (counter_traffic(kname, wl.name, profile_variant(args.state_dtype))
                if profiled else None)
@@ -863,6 +868,7 @@ def main():
                    "num_k_heads": wl.num_k_heads, "num_v_heads": wl.num_v_heads,
                    "head_k_dim": wl.head_k_dim, "head_v_dim": wl.head_v_dim,
                    "activations": wl.act, "state": args.state_dtype, "state_layout": args.layout,
+                   "intermediates": wl.intermediates,
                    "pool_slots": wl.num_slots,
                    "slot_sets": sets, "kernel": kname,
                    "block_v": info.block_v, "block_k": info.block_k,
