@@ -109,11 +109,12 @@ template <int K, int ACT>
 struct PrepPlan {
     static constexpr int THREADS = 256;
     static constexpr int P = ACT == 0 ? 2 : 1;   // bf16 parts per input element
-    // Pitch of the staged [C][K] rows (bf16).  The prep reads them as 16-byte
-    // Gram operands, 8 lanes (rows) per cycle: a pitch of 4 mod 8 dwords puts
-    // those 8 rows on distinct 4-bank groups (the state pass, which reads 8
-    // bytes of 16 rows per cycle, uses 2 mod 4 instead).
-    static constexpr int KT = K + 8;
+    // Pitch of the staged [C][K] rows (bf16).  The Gram operands are 16-byte
+    // reads, lane (g, m) taking row m at dword 4 g; on gfx950 that pattern
+    // runs at 256 B/clk per CU with a pitch of 8 mod 16 dwords and at 157
+    // B/clk with one of 4 mod 8 (measured with 8 wavefronts per CU).  The
+    // staging writes whole rows, which no pitch makes conflict.
+    static constexpr int KT = K + 16;
     static constexpr int LDB = 18;               // pitch of a 16 x 16 fp32 block (8-byte rows)
     static constexpr int BLK = 16 * LDB;         // floats per block
     static constexpr int stage_bytes = 2 * P * kC * KT * 2;
@@ -123,6 +124,7 @@ struct PrepPlan {
     static constexpr int kBatch = 4;              // v-heads whose gates are prepared at once
     static constexpr int sc = r0 + r0_bytes;      // rk, rq: [2][C]; then beta, G hi, G lo: [3][kBatch][C]
     static constexpr int bytes = sc + (2 + 3 * kBatch) * kC * 4;
+    static_assert((KT / 2) % 16 == 8 && (KT * 2) % 16 == 0, "16-byte rows, pitch 8 mod 16 dwords");
     static_assert(ACT == 0 || bytes <= 40 * 1024, "four prep workgroups per CU (bf16 inputs)");
     static_assert(bytes <= 80 * 1024, "two prep workgroups per CU (fp32 inputs)");
 };
@@ -552,9 +554,9 @@ struct StatePlan {
     static constexpr int P = ACT == 0 ? 2 : 1;
     // Row pitches of 2 mod 4 dwords: the 16 lanes that one cycle of an 8-byte
     // operand read serves (rows m16 = 0..15 at one column) then fall on 16
-    // distinct bank pairs of the 32-bank LDS.  (A pitch of 0 mod 4 dwords,
-    // as 16-byte row accesses would want, puts rows m16 and m16 + 8 on the
-    // same banks and doubles the time of every operand read.)  Rows are
+    // distinct bank pairs.  (At a pitch of 0 mod 4 dwords rows m16 and m16 + 8
+    // share banks: the operand reads, pairs of 8-byte reads 32 bytes apart,
+    // measured 156 B/clk per CU at 2 mod 4 and 85 at 4 mod 8.)  Rows are
     // therefore only 8-byte aligned, and every access to them is 8 bytes wide
     // at most.
     static constexpr int KT = K + 4;              // pitch of [C][K] (bf16)
