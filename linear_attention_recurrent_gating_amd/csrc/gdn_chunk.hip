@@ -268,16 +268,8 @@ gdn_chunk_fwd(const FusedParams p) {
                 }
                 if constexpr (ACT == 0) {
                     bf16x8 kh, kl, qh, ql;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        __bf16 hi, lo;
-                        split_bf16(xk[e], hi, lo);
-                        kh[e] = hi;
-                        kl[e] = lo;
-                        split_bf16(xq[e], hi, lo);
-                        qh[e] = hi;
-                        ql[e] = lo;
-                    }
+                    split8(xk, kh, kl);
+                    split8(xq, qh, ql);
                     lds_put8(kt + t * KT + 8 * c8, kh);
                     lds_put8(qt + t * KT + 8 * c8, qh);
                     lds_put8(kt + kC * KT + t * KT + 8 * c8, kl);

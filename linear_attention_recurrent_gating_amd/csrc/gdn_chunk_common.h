@@ -11,7 +11,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;           // tokens per chunk
@@ -24,6 +26,28 @@ __device__ __forceinline__ f32x4 mma_bf16(const bf16x8& a, const bf16x8& b, cons
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
     hi = static_cast<__bf16>(x);
     lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// split_bf16 of a pair, bit for bit: each part of the pair is one packed
+// conversion (v_cvt_pk_bf16_f32), and the hi parts are widened back from the
+// packed word (a shift and a mask): 3 VALU instructions per element where
+// converting element by element and then packing takes 4.
+__device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x2& lo) {
+    hi = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    const uint32_t w = __builtin_bit_cast(uint32_t, hi);
+    lo = __builtin_convertvector(f32x2{a - __uint_as_float(w << 16), b - __uint_as_float(w & 0xffff0000u)},
+                                 bf16x2);
+}
+
+// split_bf16 of eight elements.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    bf16x2 h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16x2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    hi = __builtin_shufflevector(__builtin_shufflevector(h[0], h[1], 0, 1, 2, 3),
+                                 __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    lo = __builtin_shufflevector(__builtin_shufflevector(l[0], l[1], 0, 1, 2, 3),
+                                 __builtin_shufflevector(l[2], l[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -40,14 +64,12 @@ struct Split4 {
 };
 
 __device__ __forceinline__ Split4 split_tile(const f32x4& x) {
+    bf16x2 h0, l0, h1, l1;
+    split_bf16x2(x[0], x[1], h0, l0);
+    split_bf16x2(x[2], x[3], h1, l1);
     Split4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 h, l;
-        split_bf16(x[e], h, l);
-        r.hi[e] = h;
-        r.lo[e] = l;
-    }
+    r.hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+    r.lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3);
     return r;
 }
 
@@ -71,17 +93,9 @@ struct Split8 {
 // of this lane: element e < 4 is row 4*(lane/16) + e of tile a, element e >= 4
 // row 4*(lane/16) + e - 4 of tile b.
 __device__ __forceinline__ Split8 operand_from_tiles(const f32x4& a, const f32x4& b) {
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     Split8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 h, l;
-        split_bf16(a[e], h, l);
-        r.hi[e] = h;
-        r.lo[e] = l;
-        split_bf16(b[e], h, l);
-        r.hi[4 + e] = h;
-        r.lo[4 + e] = l;
-    }
+    split8(x, r.hi, r.lo);
     return r;
 }
 

@@ -326,16 +326,8 @@ gdn_chunk_prep(const FusedParams p, char* ws, int B) {
             }
             if constexpr (ACT == 0) {
                 bf16x8 kh, kl, qh, ql;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    __bf16 hi, lo;
-                    split_bf16(xk[e], hi, lo);
-                    kh[e] = hi;
-                    kl[e] = lo;
-                    split_bf16(xq[e], hi, lo);
-                    qh[e] = hi;
-                    ql[e] = lo;
-                }
+                split8(xk, kh, kl);
+                split8(xq, qh, ql);
                 *reinterpret_cast<bf16x8*>(kt + t * KT + 8 * c8) = kh;
                 *reinterpret_cast<bf16x8*>(qt + t * KT + 8 * c8) = qh;
                 *reinterpret_cast<bf16x8*>(kt + kC * KT + t * KT + 8 * c8) = kl;
@@ -703,19 +695,15 @@ gdn_chunk_state(const FusedParams p, const char* ws) {
                 int t, c8;
                 stage_pos(vi, t, c8);
                 if constexpr (ACT == 0) {
-                    bf16x8 kh, kl, qh, ql;
+                    float xk[8], xq[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float xk = __uint_as_float(L.k[n][e / 4][e % 4]);
-                        const float xq = __uint_as_float(L.q[n][e / 4][e % 4]);
-                        __bf16 hi, lo;
-                        split_bf16(xk, hi, lo);
-                        kh[e] = hi;
-                        kl[e] = lo;
-                        split_bf16(xq, hi, lo);
-                        qh[e] = hi;
-                        ql[e] = lo;
+                        xk[e] = __uint_as_float(L.k[n][e / 4][e % 4]);
+                        xq[e] = __uint_as_float(L.q[n][e / 4][e % 4]);
                     }
+                    bf16x8 kh, kl, qh, ql;
+                    split8(xk, kh, kl);
+                    split8(xq, qh, ql);
                     lds_put8(kt + t * KT + 8 * c8, kh);
                     lds_put8(qt + t * KT + 8 * c8, qh);
                     lds_put8(kt + kC * KT + t * KT + 8 * c8, kl);
